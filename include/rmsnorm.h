@@ -1,0 +1,174 @@
+/*
+ * rmsnorm.h -- C ABI of the MI355X (gfx950) training-RMSNorm library.
+ *
+ * Operation (FlashInfer training-RMSNorm pages: p1 = "feat(cake_rmsnorm):
+ * opt-in non-deterministic weight gradient for the autograd RMSNorm - #8208"
+ * with its #8577 commit text, p2 = PR #8899, p3 = "fix(cake_rmsnorm_det):
+ * tighten two large-row weight-gradient accuracy edges - #8293"):
+ *
+ *   forward   rstd = 1/sqrt(mean_j u_j^2 + eps),  y = u * rstd * w
+ *             where u = x, or u = h = bf16(x + r) with the fused residual add
+ *             (p1 #8577 opening paragraph and "Key": `res` adds the BF16
+ *             output h_new).  y and h are BF16, rstd FP32.
+ *   backward  xhat = u * rstd,  c = mean_j(xhat_j * w_j * dy_j)
+ *             dx = rstd * (w * dy - xhat * c) [+ dres]   (BF16)
+ *             dw = sum over all rows of dy * xhat         (FP32)
+ *             with deterministic = 1 (fixed-order, bitwise reproducible dw)
+ *             or 0 (atomic dw, reproducible only within its error budget);
+ *             dx is bitwise the same in both modes (p1 #8208 commit message:
+ *             "dx is the same bit for bit across calls").
+ *
+ * Tensors.  Every activation tensor (x, r, h, y, dy, dres, dx) is BF16 with
+ * the logical shape [T, heads, H] and element strides (stride_t, stride_h, 1);
+ * all of them share these strides.  heads = 1 gives plain [T, H] rows
+ * (stride_t >= H).  heads > 1 gives per-head views sharing one w[H]
+ * (p1 #8577 "Key": [T,24,256] strided and [T,4,256] contiguous), and then the
+ * rows are R = T * heads.  rstd is a contiguous FP32 [R] array indexed
+ * t * heads + head.  w is [H], BF16 or FP32; dw is a contiguous FP32 [H].
+ *
+ * Memory and streams.  All pointers are device pointers owned by the caller.
+ * The library never allocates, frees or synchronises: a call validates its
+ * arguments on the host (before any HIP call), enqueues its kernels on
+ * `stream` (a hipStream_t; NULL = the default stream) and returns.
+ *
+ * Requirements checked on entry (violations return an error, nothing runs):
+ *   - H % 8 == 0 and 8 <= H <= RMSN_MAX_H                  else RMSN_ERR_UNSUPPORTED
+ *   - T >= 0, heads >= 1, R = T*heads < 2^31, eps finite >= 0
+ *   - rows do not overlap: heads == 1: stride_t >= H (or T <= 1);
+ *     heads > 1: stride_h >= H and stride_t >= heads*stride_h (or T <= 1)
+ *                                                         else RMSN_ERR_INVALID_ARG
+ *   - activation pointers and w 16-byte aligned, stride_t and stride_h
+ *     multiples of 8 elements; rstd and dw 4-byte aligned;
+ *     workspace 256-byte aligned                          else RMSN_ERR_MISALIGNED
+ * Aliasing: y may be x, residual_out may be x or residual, dx may be dy or
+ * dres (whole tensors with identical strides).  Other overlaps are undefined.
+ * Errors in a kernel launch return RMSN_ERR_HIP.  R == 0 is valid: the
+ * forward does nothing and the backward writes dw = 0.
+ */
+#ifndef RMSNORM_MI355X_H
+#define RMSNORM_MI355X_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum rmsn_status {
+    RMSN_OK = 0,
+    RMSN_ERR_INVALID_ARG = 1,
+    RMSN_ERR_UNSUPPORTED = 2,
+    RMSN_ERR_MISALIGNED = 3,
+    RMSN_ERR_WORKSPACE = 4,
+    RMSN_ERR_HIP = 5
+};
+
+enum rmsn_dtype { RMSN_W_BF16 = 0, RMSN_W_F32 = 1 };
+
+#define RMSN_MAX_H 16384
+
+/*
+ * Forward (p1 #8577 opening paragraph: "The forward returns y (BF16) and rstd
+ * (FP32)"; p1 #8577 "Key" for `res`, `w32` and the per-head views).
+ *   x            [T,heads,H] BF16 input.
+ *   residual     [T,heads,H] BF16 r, or NULL.  With r, h = bf16(x + r) (sum in
+ *                FP32, one round-to-nearest-even) is written to residual_out
+ *                and normalised in place of x.
+ *   w            [H] weight, BF16 (w_dtype = RMSN_W_BF16) or FP32 (RMSN_W_F32).
+ *   y            [T,heads,H] BF16 output y = bf16(u * rstd * w).
+ *   residual_out [T,heads,H] BF16 output h; required iff residual != NULL.
+ *   rstd         [R] FP32 output.
+ *   eps          added to the mean of squares (the pages measure eps = 1e-6).
+ *   deterministic accepted for symmetry with the backward; the forward is
+ *                the same program, bit for bit, in both modes (p1 #8577
+ *                opening paragraph: the modes "use the same forward").
+ */
+int rmsnorm_fwd(const void* x, const void* residual, const void* w, int w_dtype,
+                void* y, void* residual_out, float* rstd,
+                int64_t T, int64_t heads, int64_t H, int64_t stride_t, int64_t stride_h,
+                double eps, int deterministic, void* stream);
+
+/*
+ * Workspace bytes that rmsnorm_bwd needs for this shape (p1 #8208 page: the
+ * facade exposes backward_workspace_bytes / backward_workspace).  A pure
+ * function of its arguments; it makes no HIP call.  The size covers both
+ * modes, so one workspace serves deterministic and non-deterministic calls
+ * alike.  Returns 0 when the shape is invalid or unsupported.
+ */
+size_t rmsnorm_bwd_workspace_size(int64_t T, int64_t heads, int64_t H, int deterministic);
+
+/*
+ * Prepare a workspace for first use: zero-fills the part that the
+ * non-deterministic backward keeps between calls (a ticket and an FP64 [H]
+ * accumulator).  Every non-deterministic call leaves that part zero again, so
+ * this is needed once per fresh allocation (or after a failed call).  A
+ * workspace that is all zero bytes is already prepared.
+ */
+int rmsnorm_bwd_workspace_init(void* workspace, size_t workspace_bytes, int64_t H, void* stream);
+
+/*
+ * Backward (p1 #8577 opening paragraph: "the backward returns dx (BF16) and
+ * dw (FP32)"; p1 #8208 commit message for the deterministic flag).
+ *   dy        [T,heads,H] BF16 incoming gradient of y.
+ *   x         [T,heads,H] BF16 normalised input of the forward (h when the
+ *             forward had a residual).
+ *   rstd      [R] FP32, as written by rmsnorm_fwd.
+ *   w, w_dtype  the forward's weight.
+ *   residual  [T,heads,H] BF16 dres, the incoming gradient of h, or NULL; it
+ *             is added to dx (dx is then the gradient of both x and r).
+ *   dx        [T,heads,H] BF16 output.
+ *   dw        [H] FP32 output, overwritten (not accumulated into).
+ *   workspace at least rmsnorm_bwd_workspace_size(...) bytes, prepared once
+ *             by rmsnorm_bwd_workspace_init; must not be used by two calls
+ *             at the same time.
+ *   deterministic 1: each chunk of rows writes FP64 column partials and a
+ *             second kernel sums them in a fixed order, so dw is bitwise
+ *             reproducible for a given shape on any MI355X.
+ *             0: chunks add their FP64 partials atomically (or take the
+ *             fixed-order pair where the route table finds it faster).
+ */
+int rmsnorm_bwd(const void* dy, const void* x, const float* rstd, const void* w, int w_dtype,
+                const void* residual, void* dx, float* dw,
+                void* workspace, size_t workspace_bytes,
+                int64_t T, int64_t heads, int64_t H, int64_t stride_t, int64_t stride_h,
+                int deterministic, void* stream);
+
+/*
+ * Route inspection and override, for the route-table measurement and for
+ * tests that cover both sides of a route edge.  A route names how the
+ * backward reduces dw over rows: form (RMSN_FORM_PAIR = per-chunk FP64
+ * partials + fixed-order reduce kernel; RMSN_FORM_ATOMIC = per-chunk FP64
+ * atomics with a last-arriving block that writes dw) and rows_per_chunk.  The
+ * per-row work, and so dx, does not depend on the route.
+ */
+enum rmsn_form { RMSN_FORM_PAIR = 0, RMSN_FORM_ATOMIC = 1 };
+
+typedef struct rmsn_route {
+    int32_t form;
+    int32_t rows_per_chunk;
+} rmsn_route;
+
+/* The route rmsnorm_bwd takes for these arguments.  Returns a status. */
+int rmsnorm_bwd_route(int64_t T, int64_t heads, int64_t H, int w_dtype, int has_residual,
+                      int deterministic, rmsn_route* out);
+
+/* Workspace bytes for an explicit route (0 when invalid). */
+size_t rmsnorm_bwd_workspace_size_for_route(int64_t T, int64_t heads, int64_t H, rmsn_route route);
+
+/* rmsnorm_bwd with an explicit route.  deterministic = 1 requires the pair
+ * form (RMSN_ERR_INVALID_ARG otherwise). */
+int rmsnorm_bwd_routed(const void* dy, const void* x, const float* rstd, const void* w, int w_dtype,
+                       const void* residual, void* dx, float* dw,
+                       void* workspace, size_t workspace_bytes,
+                       int64_t T, int64_t heads, int64_t H, int64_t stride_t, int64_t stride_h,
+                       int deterministic, rmsn_route route, void* stream);
+
+/* Human-readable name of a status code (static storage). */
+const char* rmsnorm_status_string(int status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* RMSNORM_MI355X_H */

@@ -1,0 +1,253 @@
+"""Python binding of the MI355X training-RMSNorm library (librmsnorm_mi355x.so).
+
+Argument marshalling only: every step of the forward and backward runs in the
+library's HIP kernels.  The functions carry the C ABI's names
+(include/rmsnorm.h); they take torch tensors for device memory and use torch's
+current stream, and they allocate outputs with torch when none are given.
+
+The library must have been built (``python -m rmsnorm_fwd_amd.build`` or
+``__graft_entry__.build()``); there is no fallback implementation, and a
+missing library raises on first use.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "librmsnorm_mi355x.so")
+
+RMSN_OK = 0
+RMSN_ERR_INVALID_ARG = 1
+RMSN_ERR_UNSUPPORTED = 2
+RMSN_ERR_MISALIGNED = 3
+RMSN_ERR_WORKSPACE = 4
+RMSN_ERR_HIP = 5
+RMSN_W_BF16 = 0
+RMSN_W_F32 = 1
+RMSN_FORM_PAIR = 0
+RMSN_FORM_ATOMIC = 1
+RMSN_MAX_H = 16384
+
+# every symbol include/rmsnorm.h declares
+EXPORTS = (
+    "rmsnorm_fwd",
+    "rmsnorm_bwd_workspace_size",
+    "rmsnorm_bwd_workspace_init",
+    "rmsnorm_bwd",
+    "rmsnorm_bwd_route",
+    "rmsnorm_bwd_workspace_size_for_route",
+    "rmsnorm_bwd_routed",
+    "rmsnorm_status_string",
+)
+
+
+class RmsnRoute(ctypes.Structure):
+    _fields_ = [("form", ctypes.c_int32), ("rows_per_chunk", ctypes.c_int32)]
+
+
+class RmsnError(RuntimeError):
+    def __init__(self, fn, status):
+        self.status = status
+        super().__init__(f"{fn} failed: {status_string(status)} ({status})")
+
+
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    """The loaded C library (raises if it has not been built)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(f"{LIB_PATH} is missing: build the HIP library first "
+                           "(python -m rmsnorm_fwd_amd.build)")
+    L = ctypes.CDLL(LIB_PATH)
+    i64, vp, i32 = ctypes.c_int64, ctypes.c_void_p, ctypes.c_int
+    L.rmsnorm_fwd.argtypes = [vp, vp, vp, i32, vp, vp, vp, i64, i64, i64, i64, i64,
+                              ctypes.c_double, i32, vp]
+    L.rmsnorm_fwd.restype = i32
+    L.rmsnorm_bwd_workspace_size.argtypes = [i64, i64, i64, i32]
+    L.rmsnorm_bwd_workspace_size.restype = ctypes.c_size_t
+    L.rmsnorm_bwd_workspace_init.argtypes = [vp, ctypes.c_size_t, i64, vp]
+    L.rmsnorm_bwd_workspace_init.restype = i32
+    L.rmsnorm_bwd.argtypes = [vp, vp, vp, vp, i32, vp, vp, vp, vp, ctypes.c_size_t,
+                              i64, i64, i64, i64, i64, i32, vp]
+    L.rmsnorm_bwd.restype = i32
+    L.rmsnorm_bwd_route.argtypes = [i64, i64, i64, i32, i32, i32, ctypes.POINTER(RmsnRoute)]
+    L.rmsnorm_bwd_route.restype = i32
+    L.rmsnorm_bwd_workspace_size_for_route.argtypes = [i64, i64, i64, RmsnRoute]
+    L.rmsnorm_bwd_workspace_size_for_route.restype = ctypes.c_size_t
+    L.rmsnorm_bwd_routed.argtypes = [vp, vp, vp, vp, i32, vp, vp, vp, vp, ctypes.c_size_t,
+                                     i64, i64, i64, i64, i64, i32, RmsnRoute, vp]
+    L.rmsnorm_bwd_routed.restype = i32
+    L.rmsnorm_status_string.argtypes = [i32]
+    L.rmsnorm_status_string.restype = ctypes.c_char_p
+    _lib = L
+    return L
+
+
+def status_string(status: int) -> str:
+    return lib().rmsnorm_status_string(int(status)).decode()
+
+
+def _check(fn, status):
+    if status != RMSN_OK:
+        raise RmsnError(fn, status)
+
+
+# ------------------------------------------------------------- helpers ----
+
+def _torch():
+    import torch
+    return torch
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(device, stream):
+    torch = _torch()
+    s = stream if stream is not None else torch.cuda.current_stream(device)
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def geometry(t):
+    """(T, heads, H, stride_t, stride_h) of a [T,H] or [T,heads,H] tensor
+    whose last dimension is contiguous."""
+    if t.dim() == 2:
+        T, H = t.shape
+        if t.stride(1) != 1:
+            raise ValueError("the last dimension must be contiguous")
+        return T, 1, H, (t.stride(0) if T > 1 else H), H
+    if t.dim() == 3:
+        T, heads, H = t.shape
+        if t.stride(2) != 1:
+            raise ValueError("the last dimension must be contiguous")
+        sh = t.stride(1) if heads > 1 else H
+        st = t.stride(0) if T > 1 else heads * sh
+        return T, heads, H, st, sh
+    raise ValueError("expected a [T,H] or [T,heads,H] tensor")
+
+
+def _same_geometry(a, b, what):
+    if b is not None and (tuple(a.shape) != tuple(b.shape) or geometry(a) != geometry(b)):
+        raise ValueError(f"{what} must have the shape and strides of x")
+
+
+def _like(x):
+    torch = _torch()
+    return torch.empty_strided(x.shape, x.stride(), dtype=torch.bfloat16, device=x.device)
+
+
+def _w_dtype(w):
+    torch = _torch()
+    if w.dtype == torch.bfloat16:
+        return RMSN_W_BF16
+    if w.dtype == torch.float32:
+        return RMSN_W_F32
+    raise TypeError("w must be bfloat16 or float32")
+
+
+# ------------------------------------------------------------ forward ----
+
+def rmsnorm_fwd(x, w, eps: float = 1e-6, residual=None, deterministic: bool = True, *,
+                y=None, residual_out=None, rstd=None, stream=None):
+    """y, rstd (and h = x + residual) of the training RMSNorm forward.
+
+    Returns (y, rstd, residual_out); residual_out is None without a residual."""
+    torch = _torch()
+    T, heads, H, st, sh = geometry(x)
+    _same_geometry(x, residual, "residual")
+    y = _like(x) if y is None else y
+    _same_geometry(x, y, "y")
+    if residual is not None and residual_out is None:
+        residual_out = _like(x)
+    _same_geometry(x, residual_out, "residual_out")
+    if rstd is None:
+        rstd = torch.empty(T * heads, dtype=torch.float32, device=x.device)
+    st_ = lib().rmsnorm_fwd(_ptr(x), _ptr(residual), _ptr(w), _w_dtype(w), _ptr(y),
+                            _ptr(residual_out), _ptr(rstd), T, heads, H, st, sh, float(eps),
+                            int(bool(deterministic)), _stream(x.device, stream))
+    _check("rmsnorm_fwd", st_)
+    return y, rstd, residual_out
+
+
+# ----------------------------------------------------------- backward ----
+
+def rmsnorm_bwd_workspace_size(T: int, heads: int, H: int, deterministic: bool = True) -> int:
+    return int(lib().rmsnorm_bwd_workspace_size(T, heads, H, int(bool(deterministic))))
+
+
+def rmsnorm_bwd_workspace_init(workspace, H: int, stream=None):
+    st_ = lib().rmsnorm_bwd_workspace_init(_ptr(workspace), workspace.numel() * workspace.element_size(),
+                                           H, _stream(workspace.device, stream))
+    _check("rmsnorm_bwd_workspace_init", st_)
+
+
+def rmsnorm_bwd_workspace(T: int, heads: int, H: int, device, deterministic: bool = True, nbytes=None):
+    """A zero-filled (hence prepared) workspace tensor for rmsnorm_bwd."""
+    torch = _torch()
+    n = nbytes if nbytes is not None else rmsnorm_bwd_workspace_size(T, heads, H, deterministic)
+    if n == 0:
+        raise ValueError("unsupported shape")
+    return torch.zeros(n, dtype=torch.uint8, device=device)
+
+
+def rmsnorm_bwd_route(T: int, heads: int, H: int, w_dtype: int, has_residual: bool,
+                      deterministic: bool):
+    r = RmsnRoute()
+    _check("rmsnorm_bwd_route", lib().rmsnorm_bwd_route(T, heads, H, int(w_dtype), int(bool(has_residual)),
+                                                        int(bool(deterministic)), ctypes.byref(r)))
+    return int(r.form), int(r.rows_per_chunk)
+
+
+def rmsnorm_bwd_workspace_size_for_route(T: int, heads: int, H: int, route) -> int:
+    return int(lib().rmsnorm_bwd_workspace_size_for_route(T, heads, H, RmsnRoute(*route)))
+
+
+def _bwd_args(dy, x, rstd, w, residual, dx, dw):
+    torch = _torch()
+    T, heads, H, st, sh = geometry(x)
+    _same_geometry(x, dy, "dy")
+    _same_geometry(x, residual, "residual")
+    dx = _like(x) if dx is None else dx
+    _same_geometry(x, dx, "dx")
+    if dw is None:
+        dw = torch.empty(H, dtype=torch.float32, device=x.device)
+    return (T, heads, H, st, sh), dx, dw
+
+
+def rmsnorm_bwd(dy, x, rstd, w, residual=None, deterministic: bool = True, *,
+                dx=None, dw=None, workspace=None, stream=None):
+    """dx (BF16) and dw (FP32) of the training RMSNorm backward.
+
+    ``x`` is the forward's normalised input (h with a residual); ``residual``
+    is the incoming gradient of h (dres) or None.  Returns (dx, dw)."""
+    (T, heads, H, st, sh), dx, dw = _bwd_args(dy, x, rstd, w, residual, dx, dw)
+    if workspace is None:
+        workspace = rmsnorm_bwd_workspace(T, heads, H, x.device, deterministic)
+    st_ = lib().rmsnorm_bwd(_ptr(dy), _ptr(x), _ptr(rstd), _ptr(w), _w_dtype(w), _ptr(residual),
+                            _ptr(dx), _ptr(dw), _ptr(workspace),
+                            workspace.numel() * workspace.element_size(),
+                            T, heads, H, st, sh, int(bool(deterministic)), _stream(x.device, stream))
+    _check("rmsnorm_bwd", st_)
+    return dx, dw
+
+
+def rmsnorm_bwd_routed(dy, x, rstd, w, route, residual=None, deterministic: bool = True, *,
+                       dx=None, dw=None, workspace=None, stream=None):
+    """rmsnorm_bwd with an explicit (form, rows_per_chunk) route."""
+    (T, heads, H, st, sh), dx, dw = _bwd_args(dy, x, rstd, w, residual, dx, dw)
+    if workspace is None:
+        workspace = rmsnorm_bwd_workspace(T, heads, H, x.device, deterministic,
+                                          nbytes=rmsnorm_bwd_workspace_size_for_route(T, heads, H, route))
+    st_ = lib().rmsnorm_bwd_routed(_ptr(dy), _ptr(x), _ptr(rstd), _ptr(w), _w_dtype(w), _ptr(residual),
+                                   _ptr(dx), _ptr(dw), _ptr(workspace),
+                                   workspace.numel() * workspace.element_size(),
+                                   T, heads, H, st, sh, int(bool(deterministic)), RmsnRoute(*route),
+                                   _stream(x.device, stream))
+    _check("rmsnorm_bwd_routed", st_)
+    return dx, dw

@@ -1,0 +1,263 @@
+// api.cpp -- the C ABI declared in include/rmsnorm.h: argument validation
+// (host only, before any HIP call), routing, and kernel launches on the
+// caller's stream.  No allocation, no synchronisation.
+#include <hip/hip_runtime_api.h>
+
+#include <atomic>
+#include <cmath>
+#include <cstdint>
+
+#include "../../include/rmsnorm.h"
+#include "kernels.h"
+#include "layouts.h"
+#include "route.h"
+
+using namespace rmsn;
+
+namespace {
+
+constexpr int64_t kMaxRows = int64_t(1) << 30;
+
+bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
+
+struct Shape {
+    int64_t T, heads, H, st, sh, R;
+};
+
+// Shape checks shared by every entry point.
+int check_shape(int64_t T, int64_t heads, int64_t H, int64_t st, int64_t sh, Shape* out)
+{
+    if (T < 0 || heads < 1 || H < 1) return RMSN_ERR_INVALID_ARG;
+    if (H % 8 != 0 || H > RMSN_MAX_H) return RMSN_ERR_UNSUPPORTED;
+    if (T > kMaxRows / heads) return RMSN_ERR_INVALID_ARG;
+    const int64_t R = T * heads;
+    if (st < 0 || sh < 0) return RMSN_ERR_INVALID_ARG;
+    if (heads == 1) {
+        if (T > 1 && st < H) return RMSN_ERR_INVALID_ARG;
+    } else {
+        if (sh < H) return RMSN_ERR_INVALID_ARG;
+        if (T > 1 && st < heads * sh) return RMSN_ERR_INVALID_ARG;
+    }
+    if (st % 8 != 0 || (heads > 1 && sh % 8 != 0)) return RMSN_ERR_MISALIGNED;
+    *out = Shape{T, heads, H, st, sh, R};
+    return RMSN_OK;
+}
+
+std::atomic<int> g_cu_count[64];
+
+int cu_count()
+{
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+    int n = g_cu_count[dev].load(std::memory_order_relaxed);
+    if (n <= 0) {
+        if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
+        g_cu_count[dev].store(n, std::memory_order_relaxed);
+    }
+    return n;
+}
+
+int status_of(hipError_t e) { return e == hipSuccess ? RMSN_OK : RMSN_ERR_HIP; }
+
+int check_route(const Shape& s, const rmsn_route& r, int deterministic)
+{
+    if (r.form != RMSN_FORM_PAIR && r.form != RMSN_FORM_ATOMIC) return RMSN_ERR_INVALID_ARG;
+    if (deterministic && r.form != RMSN_FORM_PAIR) return RMSN_ERR_INVALID_ARG;
+    if (r.rows_per_chunk < 1) return RMSN_ERR_INVALID_ARG;
+    if (chunks_of(s.R, r.rows_per_chunk) > kMaxChunks) return RMSN_ERR_INVALID_ARG;
+    return RMSN_OK;
+}
+
+int bwd_impl(const void* dy, const void* x, const float* rstd, const void* w, int w_dtype,
+             const void* dres, void* dx, float* dw, void* workspace, size_t workspace_bytes,
+             const Shape& s, const rmsn_route& route, hipStream_t stream)
+{
+    const BwdRoute r{route.form, route.rows_per_chunk};
+    if (s.R == 0) return status_of(launch_fill_zero(dw, s.H * 4, stream));
+
+    const int layout = pick_layout(kBwdLayouts, kNumBwdLayouts, s.H);
+    BwdParams p{};
+    p.dy = static_cast<const uint16_t*>(dy);
+    p.x = static_cast<const uint16_t*>(x);
+    p.rstd = rstd;
+    p.w = w;
+    p.dres = static_cast<const uint16_t*>(dres);
+    p.dx = static_cast<uint16_t*>(dx);
+    p.dw = dw;
+    char* ws = static_cast<char*>(workspace);
+    p.ticket = reinterpret_cast<unsigned*>(ws);
+    p.acc = reinterpret_cast<double*>(ws + ws_acc_offset());
+    p.part = reinterpret_cast<double*>(ws + ws_part_offset(s.H));
+    p.stride_t = s.st;
+    p.stride_h = s.sh;
+    p.R = (int)s.R;
+    p.heads = (int)s.heads;
+    p.H = (int)s.H;
+    p.rows_per_chunk = r.rows_per_chunk;
+    p.chunks = (int)chunks_of(s.R, r.rows_per_chunk);
+    p.atomic_form = r.form == FORM_ATOMIC;
+    p.inv_h = 1.0 / (double)s.H;
+    hipError_t e = launch_bwd(layout, w_dtype == RMSN_W_F32, p, stream);
+    if (e != hipSuccess) return RMSN_ERR_HIP;
+    if (r.form == FORM_PAIR) e = launch_dw_reduce(p.part, p.chunks, p.H, dw, stream);
+    return status_of(e);
+}
+
+int check_bwd_args(const void* dy, const void* x, const float* rstd, const void* w, int w_dtype,
+                   const void* dres, const void* dx, const float* dw, const void* workspace,
+                   const Shape& s)
+{
+    if (w_dtype != RMSN_W_BF16 && w_dtype != RMSN_W_F32) return RMSN_ERR_INVALID_ARG;
+    if (!dw) return RMSN_ERR_INVALID_ARG;
+    if (!aligned(dw, 4)) return RMSN_ERR_MISALIGNED;
+    if (s.R == 0) return RMSN_OK;
+    if (!dy || !x || !rstd || !w || !dx || !workspace) return RMSN_ERR_INVALID_ARG;
+    if (!aligned(dy, 16) || !aligned(x, 16) || !aligned(w, 16) || !aligned(dx, 16) ||
+        (dres && !aligned(dres, 16)) || !aligned(rstd, 4) || !aligned(workspace, 256))
+        return RMSN_ERR_MISALIGNED;
+    return RMSN_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int rmsnorm_fwd(const void* x, const void* residual, const void* w, int w_dtype,
+                void* y, void* residual_out, float* rstd,
+                int64_t T, int64_t heads, int64_t H, int64_t stride_t, int64_t stride_h,
+                double eps, int deterministic, void* stream)
+{
+    (void)deterministic;  // the forward is one program for both modes
+    Shape s;
+    int st = check_shape(T, heads, H, stride_t, stride_h, &s);
+    if (st != RMSN_OK) return st;
+    if (w_dtype != RMSN_W_BF16 && w_dtype != RMSN_W_F32) return RMSN_ERR_INVALID_ARG;
+    if (!(std::isfinite(eps) && eps >= 0.0)) return RMSN_ERR_INVALID_ARG;
+    if (s.R == 0) return RMSN_OK;
+    if (!x || !w || !y || !rstd) return RMSN_ERR_INVALID_ARG;
+    if ((residual != nullptr) != (residual_out != nullptr)) return RMSN_ERR_INVALID_ARG;
+    if (!aligned(x, 16) || !aligned(w, 16) || !aligned(y, 16) || !aligned(rstd, 4) ||
+        (residual && (!aligned(residual, 16) || !aligned(residual_out, 16))))
+        return RMSN_ERR_MISALIGNED;
+
+    const int layout = pick_layout(kFwdLayouts, kNumFwdLayouts, s.H);
+    const Layout& L = kFwdLayouts[layout];
+    const int64_t rpi = (int64_t)slots_of(L.lpr) * L.u;
+    const int64_t iters = (s.R + rpi - 1) / rpi;
+    const int64_t cap = (int64_t)cu_count() * 8;
+    const int grid = (int)(iters < cap ? iters : cap);
+
+    FwdParams p{};
+    p.x = static_cast<const uint16_t*>(x);
+    p.r = static_cast<const uint16_t*>(residual);
+    p.w = w;
+    p.y = static_cast<uint16_t*>(y);
+    p.h = static_cast<uint16_t*>(residual_out);
+    p.rstd = rstd;
+    p.stride_t = s.st;
+    p.stride_h = s.sh;
+    p.R = (int)s.R;
+    p.heads = (int)s.heads;
+    p.H = (int)s.H;
+    p.eps = eps;
+    p.inv_h = 1.0 / (double)s.H;
+    return status_of(launch_fwd(layout, w_dtype == RMSN_W_F32, p, grid, static_cast<hipStream_t>(stream)));
+}
+
+size_t rmsnorm_bwd_workspace_size(int64_t T, int64_t heads, int64_t H, int deterministic)
+{
+    (void)deterministic;  // one layout serves both modes
+    if (T < 0 || heads < 1 || H < 1 || H % 8 != 0 || H > RMSN_MAX_H || T > kMaxRows / heads) return 0;
+    const int64_t R = T * heads;
+    size_t best = ws_part_offset(H);
+    for (int det = 0; det <= 1; ++det)
+        for (int w32 = 0; w32 <= 1; ++w32)
+            for (int res = 0; res <= 1; ++res) {
+                const size_t b = ws_bytes_for(R, H, default_bwd_route(R, H, w32 != 0, res != 0, det != 0));
+                if (b > best) best = b;
+            }
+    return best;
+}
+
+size_t rmsnorm_bwd_workspace_size_for_route(int64_t T, int64_t heads, int64_t H, rmsn_route route)
+{
+    if (T < 0 || heads < 1 || H < 1 || H % 8 != 0 || H > RMSN_MAX_H || T > kMaxRows / heads) return 0;
+    if (route.rows_per_chunk < 1 || (route.form != RMSN_FORM_PAIR && route.form != RMSN_FORM_ATOMIC)) return 0;
+    const int64_t R = T * heads;
+    if (chunks_of(R, route.rows_per_chunk) > kMaxChunks) return 0;
+    return ws_bytes_for(R, H, BwdRoute{route.form, route.rows_per_chunk});
+}
+
+int rmsnorm_bwd_workspace_init(void* workspace, size_t workspace_bytes, int64_t H, void* stream)
+{
+    if (!workspace || H < 1 || H % 8 != 0 || H > RMSN_MAX_H) return RMSN_ERR_INVALID_ARG;
+    if (!aligned(workspace, 256)) return RMSN_ERR_MISALIGNED;
+    const size_t need = ws_part_offset(H);
+    if (workspace_bytes < need) return RMSN_ERR_WORKSPACE;
+    return status_of(launch_fill_zero(workspace, (int64_t)need, static_cast<hipStream_t>(stream)));
+}
+
+int rmsnorm_bwd_route(int64_t T, int64_t heads, int64_t H, int w_dtype, int has_residual,
+                      int deterministic, rmsn_route* out)
+{
+    if (!out) return RMSN_ERR_INVALID_ARG;
+    if (w_dtype != RMSN_W_BF16 && w_dtype != RMSN_W_F32) return RMSN_ERR_INVALID_ARG;
+    if (T < 0 || heads < 1 || H < 1 || T > kMaxRows / heads) return RMSN_ERR_INVALID_ARG;
+    if (H % 8 != 0 || H > RMSN_MAX_H) return RMSN_ERR_UNSUPPORTED;
+    const BwdRoute r = default_bwd_route(T * heads, H, w_dtype == RMSN_W_F32, has_residual != 0, deterministic != 0);
+    out->form = r.form;
+    out->rows_per_chunk = r.rows_per_chunk;
+    return RMSN_OK;
+}
+
+int rmsnorm_bwd_routed(const void* dy, const void* x, const float* rstd, const void* w, int w_dtype,
+                       const void* residual, void* dx, float* dw,
+                       void* workspace, size_t workspace_bytes,
+                       int64_t T, int64_t heads, int64_t H, int64_t stride_t, int64_t stride_h,
+                       int deterministic, rmsn_route route, void* stream)
+{
+    Shape s;
+    int st = check_shape(T, heads, H, stride_t, stride_h, &s);
+    if (st != RMSN_OK) return st;
+    st = check_bwd_args(dy, x, rstd, w, w_dtype, residual, dx, dw, workspace, s);
+    if (st != RMSN_OK) return st;
+    st = check_route(s, route, deterministic);
+    if (st != RMSN_OK) return st;
+    if (s.R > 0 && workspace_bytes < ws_bytes_for(s.R, s.H, BwdRoute{route.form, route.rows_per_chunk}))
+        return RMSN_ERR_WORKSPACE;
+    return bwd_impl(dy, x, rstd, w, w_dtype, residual, dx, dw, workspace, workspace_bytes, s, route,
+                    static_cast<hipStream_t>(stream));
+}
+
+int rmsnorm_bwd(const void* dy, const void* x, const float* rstd, const void* w, int w_dtype,
+                const void* residual, void* dx, float* dw,
+                void* workspace, size_t workspace_bytes,
+                int64_t T, int64_t heads, int64_t H, int64_t stride_t, int64_t stride_h,
+                int deterministic, void* stream)
+{
+    Shape s;
+    int st = check_shape(T, heads, H, stride_t, stride_h, &s);
+    if (st != RMSN_OK) return st;
+    st = check_bwd_args(dy, x, rstd, w, w_dtype, residual, dx, dw, workspace, s);
+    if (st != RMSN_OK) return st;
+    const BwdRoute r = default_bwd_route(s.R, s.H, w_dtype == RMSN_W_F32, residual != nullptr, deterministic != 0);
+    const rmsn_route route{r.form, r.rows_per_chunk};
+    if (s.R > 0 && workspace_bytes < ws_bytes_for(s.R, s.H, r)) return RMSN_ERR_WORKSPACE;
+    return bwd_impl(dy, x, rstd, w, w_dtype, residual, dx, dw, workspace, workspace_bytes, s, route,
+                    static_cast<hipStream_t>(stream));
+}
+
+const char* rmsnorm_status_string(int status)
+{
+    switch (status) {
+    case RMSN_OK: return "ok";
+    case RMSN_ERR_INVALID_ARG: return "invalid argument";
+    case RMSN_ERR_UNSUPPORTED: return "unsupported shape (H must be a multiple of 8 and at most RMSN_MAX_H)";
+    case RMSN_ERR_MISALIGNED: return "misaligned pointer or stride";
+    case RMSN_ERR_WORKSPACE: return "workspace missing or too small";
+    case RMSN_ERR_HIP: return "HIP launch error";
+    default: return "unknown status";
+    }
+}
+
+}  // extern "C"

@@ -1,0 +1,74 @@
+// layouts.h -- how a row of H BF16 values is spread over the lanes of a
+// workgroup, for the forward and the backward kernels.  Internal to the
+// library (host and device code both read these tables).
+//
+// A row is read as H/8 vectors of 16 bytes (8 BF16 values).  A "row group"
+// of LPR lanes covers one row: lane g owns vectors g, g + LPR, ...,
+// g + (V-1)*LPR, so each load instruction of a wavefront touches consecutive
+// 16-byte vectors.  LPR <= 64 keeps a row inside one wavefront (reduced with
+// DPP and ds_swizzle only); LPR > 64 spans LPR/64 wavefronts that combine
+// their partial sums through LDS.  A workgroup has BLOCK = max(256, LPR)
+// lanes, i.e. SLOTS = BLOCK/LPR row groups, and each row group takes U rows
+// per iteration, so one iteration covers RPI = SLOTS*U rows.  The layout is
+// a function of H alone, which keeps the order of every row reduction --
+// and so y, rstd and dx -- independent of T, of the route and of the mode.
+#pragma once
+
+namespace rmsn {
+
+struct Layout {
+    int max_h;  // the layout serves H <= max_h (H % 8 == 0)
+    int lpr;    // lanes per row
+    int v;      // 16-byte vectors per lane per row
+    int u;      // rows per row group per iteration
+};
+
+// X(id, max_h, lpr, v, u)
+#define RMSN_FWD_LAYOUTS(X) \
+    X(0, 64, 8, 1, 4)       \
+    X(1, 128, 16, 1, 4)     \
+    X(2, 256, 32, 1, 4)     \
+    X(3, 512, 64, 1, 2)     \
+    X(4, 1024, 64, 2, 2)    \
+    X(5, 1536, 64, 3, 1)    \
+    X(6, 2048, 64, 4, 1)    \
+    X(7, 3072, 64, 6, 1)    \
+    X(8, 4096, 64, 8, 1)    \
+    X(9, 5120, 64, 10, 1)   \
+    X(10, 6144, 64, 12, 1)  \
+    X(11, 8192, 128, 8, 1)  \
+    X(12, 16384, 256, 8, 1)
+
+#define RMSN_BWD_LAYOUTS(X) \
+    X(0, 64, 8, 1, 2)       \
+    X(1, 128, 16, 1, 2)     \
+    X(2, 256, 32, 1, 2)     \
+    X(3, 512, 64, 1, 2)     \
+    X(4, 1024, 64, 2, 1)    \
+    X(5, 1536, 64, 3, 1)    \
+    X(6, 2048, 256, 1, 1)   \
+    X(7, 4096, 256, 2, 1)   \
+    X(8, 6144, 256, 3, 1)   \
+    X(9, 8192, 512, 2, 1)   \
+    X(10, 16384, 1024, 2, 1)
+
+#define RMSN_LAYOUT_ENTRY(id, mh, l, vv, uu) Layout{mh, l, vv, uu},
+static constexpr Layout kFwdLayouts[] = {RMSN_FWD_LAYOUTS(RMSN_LAYOUT_ENTRY)};
+static constexpr Layout kBwdLayouts[] = {RMSN_BWD_LAYOUTS(RMSN_LAYOUT_ENTRY)};
+#undef RMSN_LAYOUT_ENTRY
+
+static constexpr int kNumFwdLayouts = sizeof(kFwdLayouts) / sizeof(kFwdLayouts[0]);
+static constexpr int kNumBwdLayouts = sizeof(kBwdLayouts) / sizeof(kBwdLayouts[0]);
+
+constexpr int block_of(int lpr) { return lpr > 256 ? lpr : 256; }
+constexpr int slots_of(int lpr) { return block_of(lpr) / lpr; }
+
+// Smallest layout that covers H (tables are sorted by max_h); -1 if none.
+inline int pick_layout(const Layout* t, int n, long long H)
+{
+    for (int i = 0; i < n; ++i)
+        if (H <= t[i].max_h) return i;
+    return -1;
+}
+
+}  // namespace rmsn

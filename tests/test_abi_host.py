@@ -1,0 +1,148 @@
+"""Host-side checks of the C ABI (no GPU needed): the library loads, exports
+every function include/rmsnorm.h declares, and rejects bad arguments before
+making any HIP call; the workspace-size and route queries are pure."""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+import rmsnorm_fwd_amd as rn
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "rmsnorm.h")
+
+
+def _declared():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(rmsnorm_\w+)\s*\(", text)))
+
+
+def test_header_declarations_match_binding():
+    assert _declared() == sorted(rn.EXPORTS)
+
+
+def test_library_exports_every_declared_symbol():
+    L = rn.lib()
+    for name in _declared():
+        assert hasattr(L, name), name
+    out = subprocess.run(["nm", "-D", "--defined-only", rn.LIB_PATH], capture_output=True, text=True).stdout
+    exported = set(re.findall(r" T (\w+)$", out, flags=re.M))
+    assert set(_declared()) <= exported
+
+
+def test_library_is_gfx950_only():
+    # the offload bundle of the built library names its code-object targets
+    blob = open(rn.LIB_PATH, "rb").read()
+    targets = set(re.findall(rb"amdgcn-amd-amdhsa--(gfx[0-9a-z]+)", blob))
+    assert targets == {b"gfx950"}
+
+
+BAD = ctypes.c_void_p(0x1001)     # never dereferenced: validation rejects it first
+GOOD = ctypes.c_void_p(0x10000)   # 64 KiB aligned fake device address
+
+
+def _fwd(**kw):
+    a = dict(x=GOOD, r=None, w=GOOD, wd=0, y=GOOD, h=None, rstd=GOOD, T=4, heads=1, H=64,
+             st=64, sh=64, eps=1e-6)
+    a.update(kw)
+    return rn.lib().rmsnorm_fwd(a["x"], a["r"], a["w"], a["wd"], a["y"], a["h"], a["rstd"], a["T"],
+                                a["heads"], a["H"], a["st"], a["sh"], a["eps"], 1, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(H=12, st=12, sh=12), rn.RMSN_ERR_UNSUPPORTED),
+    (dict(H=rn.RMSN_MAX_H + 8, st=rn.RMSN_MAX_H + 8), rn.RMSN_ERR_UNSUPPORTED),
+    (dict(H=0), rn.RMSN_ERR_INVALID_ARG),
+    (dict(T=-1), rn.RMSN_ERR_INVALID_ARG),
+    (dict(heads=0), rn.RMSN_ERR_INVALID_ARG),
+    (dict(wd=7), rn.RMSN_ERR_INVALID_ARG),
+    (dict(eps=-1.0), rn.RMSN_ERR_INVALID_ARG),
+    (dict(eps=float("nan")), rn.RMSN_ERR_INVALID_ARG),
+    (dict(st=32), rn.RMSN_ERR_INVALID_ARG),                      # rows overlap
+    (dict(heads=4, st=128, sh=64), rn.RMSN_ERR_INVALID_ARG),     # tokens overlap
+    (dict(heads=4, st=256, sh=32), rn.RMSN_ERR_INVALID_ARG),     # heads overlap
+    (dict(st=68), rn.RMSN_ERR_MISALIGNED),
+    (dict(x=BAD), rn.RMSN_ERR_MISALIGNED),
+    (dict(y=BAD), rn.RMSN_ERR_MISALIGNED),
+    (dict(x=None), rn.RMSN_ERR_INVALID_ARG),
+    (dict(rstd=None), rn.RMSN_ERR_INVALID_ARG),
+    (dict(r=GOOD), rn.RMSN_ERR_INVALID_ARG),                     # residual without residual_out
+    (dict(h=GOOD), rn.RMSN_ERR_INVALID_ARG),
+    (dict(T=1 << 31), rn.RMSN_ERR_INVALID_ARG),
+])
+def test_fwd_rejects_bad_arguments(kw, status):
+    assert _fwd(**kw) == status
+
+
+def test_fwd_zero_rows_is_a_no_op():
+    assert _fwd(T=0, x=None, y=None, rstd=None) == rn.RMSN_OK
+
+
+def _bwd(**kw):
+    a = dict(dy=GOOD, x=GOOD, rstd=GOOD, w=GOOD, wd=0, dres=None, dx=GOOD, dw=GOOD, ws=GOOD,
+             wsb=1 << 30, T=4, heads=1, H=64, st=64, sh=64, det=1)
+    a.update(kw)
+    return rn.lib().rmsnorm_bwd(a["dy"], a["x"], a["rstd"], a["w"], a["wd"], a["dres"], a["dx"],
+                                a["dw"], a["ws"], a["wsb"], a["T"], a["heads"], a["H"], a["st"],
+                                a["sh"], a["det"], None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(H=20, st=20, sh=20), rn.RMSN_ERR_UNSUPPORTED),
+    (dict(wd=2), rn.RMSN_ERR_INVALID_ARG),
+    (dict(dw=None), rn.RMSN_ERR_INVALID_ARG),
+    (dict(ws=None), rn.RMSN_ERR_INVALID_ARG),
+    (dict(dy=None), rn.RMSN_ERR_INVALID_ARG),
+    (dict(dx=BAD), rn.RMSN_ERR_MISALIGNED),
+    (dict(dres=BAD), rn.RMSN_ERR_MISALIGNED),
+    (dict(ws=ctypes.c_void_p(0x10080)), rn.RMSN_ERR_MISALIGNED),  # not 256-byte aligned
+    (dict(wsb=16), rn.RMSN_ERR_WORKSPACE),
+    (dict(wsb=16, det=0), rn.RMSN_ERR_WORKSPACE),
+])
+def test_bwd_rejects_bad_arguments(kw, status):
+    assert _bwd(**kw) == status
+
+
+def test_workspace_size_is_pure_and_covers_both_modes():
+    for (T, heads, H) in [(4096, 1, 1536), (65536, 1, 4096), (131072, 1, 6144), (32768, 24, 256),
+                          (1, 1, 8), (0, 1, 64)]:
+        a = rn.rmsnorm_bwd_workspace_size(T, heads, H, True)
+        b = rn.rmsnorm_bwd_workspace_size(T, heads, H, False)
+        assert a == b == rn.rmsnorm_bwd_workspace_size(T, heads, H, True)
+        assert a > 0 and a % 256 == 0 or a > 0
+        for det in (0, 1):
+            for wd in (0, 1):
+                for res in (0, 1):
+                    route = rn.rmsnorm_bwd_route(T, heads, H, wd, res, det)
+                    need = rn.rmsnorm_bwd_workspace_size_for_route(T, heads, H, route)
+                    assert 0 < need <= a
+                    if det:
+                        assert route[0] == rn.RMSN_FORM_PAIR
+    assert rn.rmsnorm_bwd_workspace_size(10, 1, 12, True) == 0
+    assert rn.rmsnorm_bwd_workspace_size(-1, 1, 64, True) == 0
+
+
+def test_route_rows_per_chunk_depend_only_on_shape():
+    # deterministic dw is fixed by the chunking; it must not vary with anything
+    # but the shape (and never with the device's compute-unit count).
+    r1 = rn.rmsnorm_bwd_route(65536, 1, 4096, 1, 0, 1)
+    r2 = rn.rmsnorm_bwd_route(65536, 1, 4096, 1, 0, 1)
+    assert r1 == r2 and r1[1] >= 1
+
+
+def test_routed_rejects_atomic_form_in_deterministic_mode():
+    st = rn.lib().rmsnorm_bwd_routed(GOOD, GOOD, GOOD, GOOD, 0, None, GOOD, GOOD, GOOD, 1 << 30,
+                                     4, 1, 64, 64, 64, 1, rn.RmsnRoute(rn.RMSN_FORM_ATOMIC, 4), None)
+    assert st == rn.RMSN_ERR_INVALID_ARG
+    st = rn.lib().rmsnorm_bwd_routed(GOOD, GOOD, GOOD, GOOD, 0, None, GOOD, GOOD, GOOD, 1 << 30,
+                                     4, 1, 64, 64, 64, 0, rn.RmsnRoute(rn.RMSN_FORM_PAIR, 0), None)
+    assert st == rn.RMSN_ERR_INVALID_ARG
+
+
+def test_status_strings():
+    for s in range(6):
+        assert rn.status_string(s)
+    assert rn.status_string(99) == "unknown status"

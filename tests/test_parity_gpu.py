@@ -1,0 +1,78 @@
+"""GPU parity of the HIP path against the FP64 oracle at sizes the oracle
+finishes in seconds: every width layout, ragged widths, padded rows, strided
+per-head views, both weight dtypes, residual in and out, both modes."""
+import numpy as np
+import pytest
+
+from tests.helpers import Layout, run_case
+
+pytestmark = pytest.mark.gpu
+
+
+def test_config1_shape_exact():
+    # T=4096, H=1536, BF16 w, seed 0, plain rows, both modes
+    rep = run_case(Layout.plain(4096, 1536), "bf16", det_repeats=10)
+    print("config1", rep)
+
+
+# every forward / backward layout, and the widths just past each boundary
+WIDTHS = [8, 64, 72, 128, 136, 256, 264, 512, 520, 1024, 1032, 1536, 1544, 2048, 2056, 3072,
+          4096, 4104, 5120, 6144, 6152, 8192, 8200, 16384]
+
+
+@pytest.mark.parametrize("H", WIDTHS)
+@pytest.mark.parametrize("wdt", ["bf16", "f32"])
+def test_widths(H, wdt):
+    T = 37 if H >= 4096 else 301
+    rep = run_case(Layout.plain(T, H), wdt, seed=H)
+    print(H, wdt, rep)
+
+
+@pytest.mark.parametrize("H", [256, 1536, 4096, 6144])
+@pytest.mark.parametrize("wdt", ["bf16", "f32"])
+@pytest.mark.parametrize("dres", [False, True])
+def test_residual(H, wdt, dres):
+    rep = run_case(Layout.plain(257, H), wdt, res=True, dres=dres, seed=7)
+    print(H, wdt, dres, rep)
+
+
+@pytest.mark.parametrize("T", [1, 2, 3, 5, 17, 63, 64, 65, 127, 1000])
+def test_row_counts(T):
+    run_case(Layout.plain(T, 2048), "bf16", seed=T)
+    run_case(Layout.plain(T, 256), "f32", seed=T)
+
+
+def test_padded_rows():
+    run_case(Layout.plain(129, 1024, pad=64), "bf16", res=True, dres=True, seed=3)
+    run_case(Layout.plain(65, 4096, pad=8), "f32", seed=4)
+
+
+@pytest.mark.parametrize("layout", [
+    Layout.heads_view(512, 24, 256, 8192, 256),     # q slice of a [T, 8192] buffer
+    Layout.heads_view(512, 24, 256, 12288, 512),    # strides (12288, 512, 1)
+    Layout.heads_view(1024, 4, 256, 1024, 256),     # contiguous [T, 4, 256]
+    Layout.heads_view(33, 3, 1024, 4096, 1280),
+])
+@pytest.mark.parametrize("wdt", ["bf16", "f32"])
+def test_head_views(layout, wdt):
+    rep = run_case(layout, wdt, seed=11)
+    print(layout, wdt, rep)
+
+
+@pytest.mark.parametrize("family", ["normal", "outlier", "offset"])
+def test_input_families(family):
+    rep = run_case(Layout.plain(2048, 4096), "f32", family=family, seed=5)
+    print(family, rep)
+
+
+def test_zero_rows_backward_writes_zero_dw():
+    import torch
+    import rmsnorm_fwd_amd as rn
+    x = torch.empty(0, 512, dtype=torch.bfloat16, device="cuda")
+    w = torch.ones(512, dtype=torch.bfloat16, device="cuda")
+    rstd = torch.empty(0, dtype=torch.float32, device="cuda")
+    dw = torch.full((512,), 7.0, device="cuda")
+    y, r, _ = rn.rmsnorm_fwd(x, w)
+    dx, dw = rn.rmsnorm_bwd(x, x, rstd, w, dw=dw)
+    torch.cuda.synchronize()
+    assert y.numel() == 0 and int(dw.count_nonzero()) == 0
