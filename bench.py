@@ -1,0 +1,374 @@
+"""Benchmark of the MI355X training RMSNorm on one GPU.
+
+Workload (default): T=65536 rows of H=4096 BF16 values, FP32 weight
+w = 1 + 0.1 N(0,1), x and dy ~ N(0,1), eps = 1e-6, plain rows -- the shape the
+pages' headline comparison is quoted on.  A step is the pages' checkpointed
+training step "2xfwd+bwd" (forward, forward recompute, backward; p2
+"Key": op 2xfwd+bwd), here with the deterministic backward.
+
+Printed: ONE JSON line.  `value` is the step's effective HBM throughput
+(algorithmic bytes of fwd + fwd + bwd over the measured step time, back to
+back with inputs resident in HBM).  Beside it the line carries, per op and
+mode, latency with L2 and the 256 MB last-level cache flushed before every
+launch (the pages' protocol: cold L2, median of many launches), the
+per-kernel roofline of the dominant kernel from HIP events, and the CPU
+oracle timed on the host as a baseline.
+
+Algorithmic bytes (what the operation must move; workspace traffic excluded):
+  fwd = 4 R H (+4 R H with a residual) + 4 R + sw H
+  bwd = 6 R H (+2 R H with dres) + 4 R + sw H + 4 H,  sw = 2 (BF16 w) or 4 (FP32 w)
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import statistics
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+PEAK_GBS = 8000.0  # MI355X HBM3E
+EPS = 1e-6
+
+WORKLOADS = {
+    # name: (T, heads, H, stride_t, stride_h, w dtype, residual)
+    "T65536_H4096_w32": (65536, 1, 4096, 4096, 4096, "f32", False),
+    "T4096_H1536": (4096, 1, 1536, 1536, 1536, "bf16", False),
+    "T131072_H6144_res": (131072, 1, 6144, 6144, 6144, "bf16", True),
+    "T131072_H6144_res_w32": (131072, 1, 6144, 6144, 6144, "f32", True),
+    "T32768_24x256_s8192": (32768, 24, 256, 8192, 256, "bf16", False),
+    "T32768_4x256": (32768, 4, 256, 1024, 256, "bf16", False),
+    "T65536_H5120": (65536, 1, 5120, 5120, 5120, "bf16", False),
+    "T65536_H5120_w32": (65536, 1, 5120, 5120, 5120, "f32", False),
+    "T32768_H5120": (32768, 1, 5120, 5120, 5120, "bf16", False),
+    "T19968_H5120": (19968, 1, 5120, 5120, 5120, "bf16", False),
+    "T6144_H5120": (6144, 1, 5120, 5120, 5120, "bf16", False),
+    "T2048_H5120": (2048, 1, 5120, 5120, 5120, "bf16", False),
+}
+DEFAULT_WORKLOAD = "T65536_H4096_w32"
+
+
+def fwd_bytes(R, H, sw, res):
+    return (8 if res else 4) * R * H + 4 * R + sw * H
+
+
+def bwd_bytes(R, H, sw, dres):
+    return (8 if dres else 6) * R * H + 4 * R + sw * H + 4 * H
+
+
+def log(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def percentile(v, q):
+    return float(np.percentile(np.asarray(v), q))
+
+
+class Workload:
+    def __init__(self, name, seed=0):
+        import torch
+
+        import rmsnorm_fwd_amd as rn
+        import synth
+
+        self.name = name
+        T, heads, H, st, sh, wdt, res = WORKLOADS[name]
+        self.T, self.heads, self.H, self.st, self.sh, self.wdt, self.res = T, heads, H, st, sh, wdt, res
+        self.R = T * heads
+        self.sw = 4 if wdt == "f32" else 2
+        dev = "cuda"
+        t0 = time.time()
+        self.x_h = synth.rows(seed, "x", 0, self.R, H)
+        self.dy_h = synth.rows(seed, "dy", 0, self.R, H)
+        self.r_h = synth.rows(seed, "r", 0, self.R, H) if res else None
+        self.w_h = synth.weight(seed, H, wdt)
+        log(f"generated inputs in {time.time() - t0:.1f}s")
+
+        def place(rows):
+            n = (T - 1) * st + (heads - 1) * sh + H
+            buf = torch.zeros(n, dtype=torch.bfloat16, device=dev)
+            v = self.view(buf)
+            v.copy_(torch.from_numpy(rows.view(np.int16)).view(torch.bfloat16).to(dev).view(v.shape))
+            return buf
+
+        self.view = lambda buf: (torch.as_strided(buf, (T, H), (st, 1)) if heads == 1 else
+                                 torch.as_strided(buf, (T, heads, H), (st, sh, 1)))
+        self.x = self.view(place(self.x_h))
+        self.dy = self.view(place(self.dy_h))
+        self.r = self.view(place(self.r_h)) if res else None
+        self.w = (torch.from_numpy(self.w_h).to(dev) if wdt == "f32" else
+                  torch.from_numpy(self.w_h.view(np.int16)).view(torch.bfloat16).to(dev))
+        self.y = self.view(place(self.x_h))
+        self.h = self.view(place(self.x_h)) if res else None
+        self.dx = self.view(place(self.x_h))
+        self.rstd = torch.empty(self.R, dtype=torch.float32, device=dev)
+        self.dw = torch.empty(H, dtype=torch.float32, device=dev)
+        self.ws = rn.rmsnorm_bwd_workspace(T, heads, H, dev)
+        self.fwd_bytes = fwd_bytes(self.R, H, self.sw, res)
+        self.bwd_bytes = bwd_bytes(self.R, H, self.sw, False)
+        self.step_bytes = 2 * self.fwd_bytes + self.bwd_bytes
+        self.rn = rn
+
+    def fwd(self):
+        self.rn.rmsnorm_fwd(self.x, self.w, EPS, residual=self.r, y=self.y, residual_out=self.h,
+                            rstd=self.rstd)
+
+    def bwd(self, det=True):
+        u = self.h if self.res else self.x
+        self.rn.rmsnorm_bwd(self.dy, u, self.rstd, self.w, deterministic=det, dx=self.dx, dw=self.dw,
+                            workspace=self.ws)
+
+    def step(self, det=True):
+        self.fwd()
+        self.fwd()
+        self.bwd(det)
+
+
+def time_cold(fn, reps, flush_buf):
+    """Median/p10/p90 microseconds of fn with L2 and last-level cache flushed
+    before each launch (a 1 GiB write on the same stream, outside the events)."""
+    import torch
+
+    ts = []
+    for _ in range(reps):
+        flush_buf.fill_(1)
+        a = torch.cuda.Event(enable_timing=True)
+        b = torch.cuda.Event(enable_timing=True)
+        a.record()
+        fn()
+        b.record()
+        b.synchronize()
+        ts.append(a.elapsed_time(b) * 1e3)
+    return {"median_us": statistics.median(ts), "p10_us": percentile(ts, 10), "p90_us": percentile(ts, 90)}
+
+
+def time_warm(fn, reps):
+    """Average microseconds per launch of fn, launches back to back, bracketed
+    by HIP events on the library's stream."""
+    import torch
+
+    a = torch.cuda.Event(enable_timing=True)
+    b = torch.cuda.Event(enable_timing=True)
+    a.record()
+    for _ in range(reps):
+        fn()
+    b.record()
+    b.synchronize()
+    return a.elapsed_time(b) * 1e3 / reps
+
+
+def cpu_baseline(wl: Workload, min_seconds=10.0, max_seconds=30.0):
+    """The oracle (FP64, OpenMP) on the host: fwd + fwd + bwd over a bounded
+    sample of the workload's rows, as GB/s of the same byte model.  The
+    sample is the whole workload when one step takes under ~10 s, else the
+    leading rows; the step repeats until about 10 s of work is done."""
+    import oracle
+
+    nthreads = oracle.num_threads()
+    probe_rows = min(wl.R, 2048)
+    t0 = time.time()
+    _step_oracle(wl, probe_rows)
+    per_row = (time.time() - t0) / probe_rows
+    rows = int(min(wl.R, max(probe_rows, 10.0 / max(per_row, 1e-9))))
+    reps = []
+    t_start = time.time()
+    while (time.time() - t_start) < min_seconds or len(reps) < 3:
+        t0 = time.time()
+        _step_oracle(wl, rows)
+        reps.append(time.time() - t0)
+        if time.time() - t_start > max_seconds:
+            break
+    sec = statistics.median(reps)
+    sample_bytes = 2 * fwd_bytes(rows, wl.H, wl.sw, wl.res) + bwd_bytes(rows, wl.H, wl.sw, False)
+    return {"value": sample_bytes / sec / 1e9, "unit": "GB/s", "cores": nthreads, "kind": "oracle",
+            "sample": f"2xfwd+bwd over rows 0..{rows - 1} of {wl.R} (H={wl.H}), median of {len(reps)} "
+                      f"repeats, {sec:.2f} s per step, {time.time() - t_start:.1f} s in all",
+            "step_seconds": sec, "rows": rows}
+
+
+def profiled_traffic(workload, kernel):
+    """HBM bytes per launch of `kernel` from the committed rocprofv3 summary
+    for this workload, or None if there is none or the kernel's sources have
+    changed since it was taken."""
+    import hashlib
+    import re
+
+    path = os.path.join(ROOT, "profiles", f"rmsnorm_kernels_{workload}.md")
+    if not os.path.exists(path):
+        return None
+    m = re.search(r"```json\n(.*?)\n```", open(path).read(), re.S)
+    if not m:
+        return None
+    rec = json.loads(m.group(1)).get("kernels", {}).get(kernel)
+    if not rec:
+        return None
+    srcs = {"fwd_kernel": ["fwd.hip", "device_common.h", "layouts.h"],
+            "bwd_kernel": ["bwd.hip", "device_common.h", "layouts.h"]}[kernel]
+    h = hashlib.sha256()
+    for f in srcs:
+        with open(os.path.join(ROOT, "rmsnorm_fwd_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return rec["traffic_bytes"] if h.hexdigest()[:16] == rec["source_hash"] else None
+
+
+def _step_oracle(wl, rows):
+    import oracle
+
+    H = wl.H
+    x = _rows_view(wl.x_h, rows)
+    r = _rows_view(wl.r_h, rows) if wl.res else None
+    dy = _rows_view(wl.dy_h, rows)
+    oracle.fwd_bf16(x, wl.w_h, EPS, r)
+    y, h, rstd = oracle.fwd_bf16(x, wl.w_h, EPS, r)
+    u = h if wl.res else x
+    oracle.bwd_bf16(u, dy, wl.w_h, rstd.astype(np.float32))
+    return H
+
+
+def _rows_view(a, rows):
+    return a[:rows] if a is not None else None
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default=DEFAULT_WORKLOAD, choices=sorted(WORKLOADS))
+    ap.add_argument("--cold-reps", type=int, default=60, help="launches per op for the cache-flushed latency")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--profile", action="store_true",
+                    help="only warmup + timed steps (for rocprofv3 runs), no per-op extras")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="also run a plain 1 GiB device copy (reference for HBM counter scaling)")
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(dw would need one all-reduce of H values; see the design notes). Run with --gpus 1.",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    if not torch.cuda.is_available():
+        print("no GPU visible", file=sys.stderr)
+        sys.exit(3)
+    import rmsnorm_fwd_amd as rn
+
+    rn.lib()  # fail loudly if the HIP library is not built
+    wl = Workload(args.workload)
+    log(f"workload {wl.name}: R={wl.R} H={wl.H} w={wl.wdt} res={wl.res}")
+
+    if args.copy_calibration:
+        src = torch.empty(1 << 29, dtype=torch.int16, device="cuda").fill_(3)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        log("copy calibration: 3 x copy of 1 GiB done")
+
+    # warmup + timed steps (deterministic backward), back to back
+    for _ in range(args.warmup):
+        wl.step(True)
+    torch.cuda.synchronize()
+    log(f"warmup {args.warmup} steps done")
+    t0 = time.perf_counter()
+    ev0 = torch.cuda.Event(enable_timing=True)
+    ev1 = torch.cuda.Event(enable_timing=True)
+    ev0.record()
+    for _ in range(args.steps):
+        wl.step(True)
+    ev1.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_per_step = ev0.elapsed_time(ev1) / args.steps
+    value = wl.step_bytes / (ms_per_step * 1e-3) / 1e9
+    log(f"timed {args.steps} steps: {ms_per_step * 1e3:.1f} us/step, {value:.0f} GB/s (wall {wall:.3f}s)")
+
+    out = {
+        "metric": "RMSNorm fwd/bwd/2xfwd+bwd us and effective HBM GB/s (% of peak) at [T,H]",
+        "value": round(value, 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16 storage; fp32/fp64 accumulation",
+        "data": "synthetic (seeded N(0,1) x and dy, w = 1 + 0.1 N(0,1))",
+        "config": {"workload": wl.name, "T": wl.T, "heads": wl.heads, "H": wl.H, "w_dtype": wl.wdt,
+                   "residual": wl.res, "step": "fwd + fwd (recompute) + bwd (deterministic)",
+                   "step_bytes": wl.step_bytes, "pct_of_peak": round(100 * value / PEAK_GBS, 2)},
+    }
+
+    if not args.profile:
+        # per-op latency, cold caches
+        flush = torch.empty(1 << 28, dtype=torch.float32, device="cuda")  # 1 GiB
+        ops = {
+            "fwd": (wl.fwd, wl.fwd_bytes),
+            "bwd_det": (lambda: wl.bwd(True), wl.bwd_bytes),
+            "bwd_nondet": (lambda: wl.bwd(False), wl.bwd_bytes),
+            "step_det": (lambda: wl.step(True), wl.step_bytes),
+            "step_nondet": (lambda: wl.step(False), wl.step_bytes),
+        }
+        lat = {}
+        for name, (fn, nbytes) in ops.items():
+            for _ in range(3):
+                fn()
+            c = time_cold(fn, args.cold_reps, flush)
+            c["gbs"] = round(nbytes / (c["median_us"] * 1e-6) / 1e9, 1)
+            c["pct_peak"] = round(100 * c["gbs"] / PEAK_GBS, 2)
+            c["bytes"] = nbytes
+            for k in ("median_us", "p10_us", "p90_us"):
+                c[k] = round(c[k], 2)
+            lat[name] = c
+            log(f"cold {name}: {c['median_us']:.1f} us  {c['gbs']:.0f} GB/s ({c['pct_peak']:.1f}%)")
+        out["latency_cold"] = lat
+
+        # roofline of the dominant kernels: per-launch duration from HIP events
+        # around back-to-back launches on the stream the library uses
+        fwd_us = time_warm(wl.fwd, 40)
+        bwd_nd_us = time_warm(lambda: wl.bwd(False), 40)
+        bwd_d_us = time_warm(lambda: wl.bwd(True), 40)
+        # The forward kernel runs twice per step and takes the larger share
+        # of it; the backward (row kernel + fixed-order dw reduce) is shown
+        # beside it.
+        fwd_gbs = wl.fwd_bytes / (fwd_us * 1e-6) / 1e9
+        out["roofline"] = {"bound": "hbm", "kernel": "fwd_kernel", "achieved": round(fwd_gbs, 1),
+                           "peak": PEAK_GBS, "unit": "GB/s", "frac": round(fwd_gbs / PEAK_GBS, 4),
+                           "traffic": profiled_traffic(wl.name, "fwd_kernel"),
+                           "us_per_launch": round(fwd_us, 2), "bytes_per_launch": wl.fwd_bytes}
+        bwd_gbs = wl.bwd_bytes / (bwd_d_us * 1e-6) / 1e9
+        out["roofline_bwd"] = {"bound": "hbm", "kernel": "bwd_kernel + dw_reduce_kernel (deterministic)",
+                               "achieved": round(bwd_gbs, 1), "peak": PEAK_GBS, "unit": "GB/s",
+                               "frac": round(bwd_gbs / PEAK_GBS, 4),
+                               "traffic_row_kernel": profiled_traffic(wl.name, "bwd_kernel"),
+                               "us_per_call": round(bwd_d_us, 2), "bytes_per_call": wl.bwd_bytes,
+                               "nondet_us_per_call": round(bwd_nd_us, 2)}
+        log(f"warm fwd {fwd_us:.1f} us, bwd nondet {bwd_nd_us:.1f} us, bwd det {bwd_d_us:.1f} us")
+        route = {}
+        for det in (1, 0):
+            f, chunks = rn.rmsnorm_bwd_route(wl.T, wl.heads, wl.H, 1 if wl.wdt == "f32" else 0, wl.res, det)
+            route["det" if det else "nondet"] = {"form": "pair" if f == 0 else "atomic", "chunks": chunks}
+        out["route"] = route
+
+        if not args.no_cpu_baseline:
+            t0 = time.time()
+            out["cpu_baseline"] = cpu_baseline(wl)
+            log(f"cpu baseline: {out['cpu_baseline']['value']:.2f} GB/s on {out['cpu_baseline']['cores']} "
+                f"threads ({time.time() - t0:.1f}s)")
+
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -136,17 +136,23 @@ int rmsnorm_bwd(const void* dy, const void* x, const float* rstd, const void* w,
 
 /*
  * Route inspection and override, for the route-table measurement and for
- * tests that cover both sides of a route edge.  A route names how the
- * backward reduces dw over rows: form (RMSN_FORM_PAIR = per-chunk FP64
- * partials + fixed-order reduce kernel; RMSN_FORM_ATOMIC = per-chunk FP64
- * atomics with a last-arriving block that writes dw) and rows_per_chunk.  The
- * per-row work, and so dx, does not depend on the route.
+ * tests that cover both sides of a route edge (p3 #8293 commit message: the
+ * pairs test covers both sides of the edges).  A route names how the
+ * backward reduces dw over rows:
+ *   form   RMSN_FORM_PAIR: each of `chunks` workgroups writes an FP64 column
+ *          partial to the workspace and a second kernel sums them in a fixed
+ *          order (deterministic); RMSN_FORM_ATOMIC: the workgroups add their
+ *          partials to an FP64 accumulator atomically and the last one to
+ *          finish writes dw (one launch; order of additions not fixed).
+ *   chunks number of workgroups of the row kernel, 1 .. 65536; workgroup c
+ *          takes the row groups c, c + chunks, c + 2*chunks, ...
+ * The per-row work, and so dx, does not depend on the route.
  */
 enum rmsn_form { RMSN_FORM_PAIR = 0, RMSN_FORM_ATOMIC = 1 };
 
 typedef struct rmsn_route {
     int32_t form;
-    int32_t rows_per_chunk;
+    int32_t chunks;
 } rmsn_route;
 
 /* The route rmsnorm_bwd takes for these arguments.  Returns a status. */

@@ -43,7 +43,7 @@ EXPORTS = (
 
 
 class RmsnRoute(ctypes.Structure):
-    _fields_ = [("form", ctypes.c_int32), ("rows_per_chunk", ctypes.c_int32)]
+    _fields_ = [("form", ctypes.c_int32), ("chunks", ctypes.c_int32)]
 
 
 class RmsnError(RuntimeError):
@@ -201,7 +201,7 @@ def rmsnorm_bwd_route(T: int, heads: int, H: int, w_dtype: int, has_residual: bo
     r = RmsnRoute()
     _check("rmsnorm_bwd_route", lib().rmsnorm_bwd_route(T, heads, H, int(w_dtype), int(bool(has_residual)),
                                                         int(bool(deterministic)), ctypes.byref(r)))
-    return int(r.form), int(r.rows_per_chunk)
+    return int(r.form), int(r.chunks)
 
 
 def rmsnorm_bwd_workspace_size_for_route(T: int, heads: int, H: int, route) -> int:
@@ -239,7 +239,7 @@ def rmsnorm_bwd(dy, x, rstd, w, residual=None, deterministic: bool = True, *,
 
 def rmsnorm_bwd_routed(dy, x, rstd, w, route, residual=None, deterministic: bool = True, *,
                        dx=None, dw=None, workspace=None, stream=None):
-    """rmsnorm_bwd with an explicit (form, rows_per_chunk) route."""
+    """rmsnorm_bwd with an explicit (form, chunks) route."""
     (T, heads, H, st, sh), dx, dw = _bwd_args(dy, x, rstd, w, residual, dx, dw)
     if workspace is None:
         workspace = rmsnorm_bwd_workspace(T, heads, H, x.device, deterministic,

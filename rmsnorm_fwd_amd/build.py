@@ -15,7 +15,7 @@ CSRC = os.path.join(HERE, "csrc")
 ROOT = os.path.dirname(HERE)
 LIB = os.path.join(HERE, "librmsnorm_mi355x.so")
 BUILD_DIR = os.path.join(HERE, "_build")
-SOURCES = ["kernels.hip", "api.cpp", "route.cpp"]
+SOURCES = ["fwd.hip", "bwd.hip", "api.cpp", "route.cpp"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 COMMON = ["-O3", "-std=c++17", "-fPIC", "--offload-arch=gfx950",

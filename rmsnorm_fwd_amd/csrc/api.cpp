@@ -63,8 +63,8 @@ int check_route(const Shape& s, const rmsn_route& r, int deterministic)
 {
     if (r.form != RMSN_FORM_PAIR && r.form != RMSN_FORM_ATOMIC) return RMSN_ERR_INVALID_ARG;
     if (deterministic && r.form != RMSN_FORM_PAIR) return RMSN_ERR_INVALID_ARG;
-    if (r.rows_per_chunk < 1) return RMSN_ERR_INVALID_ARG;
-    if (chunks_of(s.R, r.rows_per_chunk) > kMaxChunks) return RMSN_ERR_INVALID_ARG;
+    (void)s;
+    if (r.chunks < 1 || r.chunks > kMaxChunks) return RMSN_ERR_INVALID_ARG;
     return RMSN_OK;
 }
 
@@ -72,7 +72,7 @@ int bwd_impl(const void* dy, const void* x, const float* rstd, const void* w, in
              const void* dres, void* dx, float* dw, void* workspace, size_t workspace_bytes,
              const Shape& s, const rmsn_route& route, hipStream_t stream)
 {
-    const BwdRoute r{route.form, route.rows_per_chunk};
+    const BwdRoute r{route.form, route.chunks};
     if (s.R == 0) return status_of(launch_fill_zero(dw, s.H * 4, stream));
 
     const int layout = pick_layout(kBwdLayouts, kNumBwdLayouts, s.H);
@@ -93,8 +93,7 @@ int bwd_impl(const void* dy, const void* x, const float* rstd, const void* w, in
     p.R = (int)s.R;
     p.heads = (int)s.heads;
     p.H = (int)s.H;
-    p.rows_per_chunk = r.rows_per_chunk;
-    p.chunks = (int)chunks_of(s.R, r.rows_per_chunk);
+    p.chunks = r.chunks;
     p.atomic_form = r.form == FORM_ATOMIC;
     p.inv_h = 1.0 / (double)s.H;
     hipError_t e = launch_bwd(layout, w_dtype == RMSN_W_F32, p, stream);
@@ -144,7 +143,7 @@ int rmsnorm_fwd(const void* x, const void* residual, const void* w, int w_dtype,
     const Layout& L = kFwdLayouts[layout];
     const int64_t rpi = (int64_t)slots_of(L.lpr) * L.u;
     const int64_t iters = (s.R + rpi - 1) / rpi;
-    const int64_t cap = (int64_t)cu_count() * 8;
+    const int64_t cap = (int64_t)cu_count() * 16;  // measured: 16 per CU best or tied at T >= 65536
     const int grid = (int)(iters < cap ? iters : cap);
 
     FwdParams p{};
@@ -182,10 +181,9 @@ size_t rmsnorm_bwd_workspace_size(int64_t T, int64_t heads, int64_t H, int deter
 size_t rmsnorm_bwd_workspace_size_for_route(int64_t T, int64_t heads, int64_t H, rmsn_route route)
 {
     if (T < 0 || heads < 1 || H < 1 || H % 8 != 0 || H > RMSN_MAX_H || T > kMaxRows / heads) return 0;
-    if (route.rows_per_chunk < 1 || (route.form != RMSN_FORM_PAIR && route.form != RMSN_FORM_ATOMIC)) return 0;
-    const int64_t R = T * heads;
-    if (chunks_of(R, route.rows_per_chunk) > kMaxChunks) return 0;
-    return ws_bytes_for(R, H, BwdRoute{route.form, route.rows_per_chunk});
+    if (route.chunks < 1 || route.chunks > kMaxChunks) return 0;
+    if (route.form != RMSN_FORM_PAIR && route.form != RMSN_FORM_ATOMIC) return 0;
+    return ws_bytes_for(T * heads, H, BwdRoute{route.form, route.chunks});
 }
 
 int rmsnorm_bwd_workspace_init(void* workspace, size_t workspace_bytes, int64_t H, void* stream)
@@ -206,7 +204,7 @@ int rmsnorm_bwd_route(int64_t T, int64_t heads, int64_t H, int w_dtype, int has_
     if (H % 8 != 0 || H > RMSN_MAX_H) return RMSN_ERR_UNSUPPORTED;
     const BwdRoute r = default_bwd_route(T * heads, H, w_dtype == RMSN_W_F32, has_residual != 0, deterministic != 0);
     out->form = r.form;
-    out->rows_per_chunk = r.rows_per_chunk;
+    out->chunks = r.chunks;
     return RMSN_OK;
 }
 
@@ -223,7 +221,7 @@ int rmsnorm_bwd_routed(const void* dy, const void* x, const float* rstd, const v
     if (st != RMSN_OK) return st;
     st = check_route(s, route, deterministic);
     if (st != RMSN_OK) return st;
-    if (s.R > 0 && workspace_bytes < ws_bytes_for(s.R, s.H, BwdRoute{route.form, route.rows_per_chunk}))
+    if (s.R > 0 && workspace_bytes < ws_bytes_for(s.R, s.H, BwdRoute{route.form, route.chunks}))
         return RMSN_ERR_WORKSPACE;
     return bwd_impl(dy, x, rstd, w, w_dtype, residual, dx, dw, workspace, workspace_bytes, s, route,
                     static_cast<hipStream_t>(stream));
@@ -241,7 +239,7 @@ int rmsnorm_bwd(const void* dy, const void* x, const float* rstd, const void* w,
     st = check_bwd_args(dy, x, rstd, w, w_dtype, residual, dx, dw, workspace, s);
     if (st != RMSN_OK) return st;
     const BwdRoute r = default_bwd_route(s.R, s.H, w_dtype == RMSN_W_F32, residual != nullptr, deterministic != 0);
-    const rmsn_route route{r.form, r.rows_per_chunk};
+    const rmsn_route route{r.form, r.chunks};
     if (s.R > 0 && workspace_bytes < ws_bytes_for(s.R, s.H, r)) return RMSN_ERR_WORKSPACE;
     return bwd_impl(dy, x, rstd, w, w_dtype, residual, dx, dw, workspace, workspace_bytes, s, route,
                     static_cast<hipStream_t>(stream));

@@ -1,0 +1,313 @@
+// bwd.hip -- backward kernels of the training RMSNorm on gfx950.
+//
+//   xhat = u * rstd,  c = mean(xhat * w * dy)
+//   dx   = bf16(rstd * (w * dy - xhat * c) [+ dres])
+//   dw   = sum over rows of dy * xhat
+// (FlashInfer training-RMSNorm pages: p1 #8577 opening paragraph; dw is
+// compared against FP64 at the kernel's FP32 rstd, p1 #8208 commit message.)
+//
+// Row kernel.  Workgroup c of `chunks` takes every chunks-th group of rows
+// (its "chunk"); a row group of LPR lanes owns a row, each lane V 16-byte
+// vectors of it.  Per element:
+// p = x*dy is exact in FP32 (two 8-bit significands) and is widened to FP64;
+// p*w (<= 24 + 16 bits) and p*rstd (24 + 16 bits) are exact in FP64, so the
+// row dot S = sum(x*w*dy) and the dw column sums round only in their FP64
+// additions.  dx = rstd*(w*dy) - x*(rstd^3 S / H) is formed in FP64 and
+// rounded to FP32, then BF16 (within one BF16 unit of the exact value).  The
+// row dot's order depends only on H, so dx is the same in both modes and for
+// every chunking.  The weights live in registers as FP64 (0 for vectors a
+// lane does not own).
+//
+// dw.  Each lane keeps FP64 column sums over the chunk's rows in registers;
+// row groups of one workgroup are added in LDS in slot order.  The chunk sum
+// then goes
+//   pair form:   to row `chunk` of a workspace [chunks, H] (FP64), summed by
+//                dw_reduce_kernel in a fixed order -- deterministic;
+//   atomic form: into an FP64 [H] accumulator by atomic add; the workgroup
+//                that draws the last arrival ticket writes dw and zeroes the
+//                accumulator and ticket -- one launch, no waiting.
+#include "device_common.h"
+#include "kernels.h"
+
+
+namespace rmsn {
+
+// One iteration's rows of a row group: addresses, rstd and the x / dy vectors.
+template <int U, int V>
+struct BwdTile {
+    bool ok[U];
+    int64_t off[U];
+    double rho[U];
+    uint4 xv[U][V], dv[U][V];
+};
+
+template <int U, int V, int SLOTS>
+__device__ __forceinline__ void bwd_load(BwdTile<U, V>& t, const BwdParams& p, const LaneVectors<V>& lv,
+                                         int base, int slot, int row1)
+{
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+        const int row = base + u * SLOTS + slot;
+        t.ok[u] = row < row1;
+        const int rr = t.ok[u] ? row : row1 - 1;  // rows past the end re-read the last row
+        t.off[u] = row_offset(rr, p.heads, p.stride_t, p.stride_h);
+        t.rho[u] = t.ok[u] ? (double)p.rstd[rr] : 0.0;  // ... and add nothing to dw
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u)
+#pragma unroll
+        for (int v = 0; v < V; ++v) {
+            t.xv[u][v] = ld16_stream(p.x + t.off[u] + lv.col[v]);
+            t.dv[u][v] = ld16_stream(p.dy + t.off[u] + lv.col[v]);
+        }
+}
+
+template <int LPR, int V, int U, bool WF32, bool DRES>
+__global__ void __launch_bounds__(block_of(LPR)) bwd_kernel(BwdParams p)
+{
+    constexpr int BLOCK = block_of(LPR);
+    constexpr int SLOTS = BLOCK / LPR;
+    constexpr int W = LPR > 64 ? LPR / 64 : 1;
+    constexpr int RPI = SLOTS * U;
+    __shared__ double red[2][RPI][W];
+    __shared__ int last_block;
+    extern __shared__ double slot_part[];  // [SLOTS][H] when SLOTS > 1
+
+    const int tid = threadIdx.x;
+    const int g = tid % LPR;
+    const int slot = tid / LPR;
+    const int H = p.H;
+    const LaneVectors<V> lv(g, LPR, H >> 3);
+    const int chunk = blockIdx.x;
+    // Workgroup `chunk` takes the row groups chunk, chunk + chunks, ...:
+    // at any moment all workgroups stream neighbouring rows, which keeps the
+    // HBM pages they touch together (measured: 1.1-1.25x over contiguous
+    // chunks of rows on MI355X).
+    const int first = chunk * RPI;
+    const int step = p.chunks * RPI;
+    const int row1 = p.R;
+
+    double w64[V][8];
+#pragma unroll
+    for (int v = 0; v < V; ++v) {
+        float wv[8];
+        if constexpr (WF32) {
+            const float4* q = reinterpret_cast<const float4*>(static_cast<const float*>(p.w) + lv.col[v]);
+            const float4 a = q[0], b = q[1];
+            wv[0] = a.x; wv[1] = a.y; wv[2] = a.z; wv[3] = a.w;
+            wv[4] = b.x; wv[5] = b.y; wv[6] = b.z; wv[7] = b.w;
+        } else {
+            unpack8(ld16(static_cast<const uint16_t*>(p.w) + lv.col[v]), wv);
+        }
+#pragma unroll
+        for (int e = 0; e < 8; ++e) w64[v][e] = lv.ok[v] ? (double)wv[e] : 0.0;
+    }
+
+    double acc[V][8];
+#pragma unroll
+    for (int v = 0; v < V; ++v)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) acc[v][e] = 0.0;
+
+    BwdTile<U, V> cur;
+    int it = 0;
+    for (int base = first; base < row1; base += step, ++it) {
+        bwd_load<U, V, SLOTS>(cur, p, lv, base, slot, row1);
+        const bool* ok = cur.ok;
+        const int64_t* off = cur.off;
+        const double* rho = cur.rho;
+        uint4 (&xv)[U][V] = cur.xv;
+        uint4 (&dv)[U][V] = cur.dv;
+        double S[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            S[u] = 0.0;
+#pragma unroll
+            for (int v = 0; v < V; ++v) {
+                float xf[8], df[8];
+                unpack8(xv[u][v], xf);
+                unpack8(dv[u][v], df);
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    const double pd = (double)(xf[e] * df[e]);
+                    acc[v][e] = __builtin_fma(pd, rho[u], acc[v][e]);
+                    S[u] = __builtin_fma(pd, w64[v][e], S[u]);
+                }
+            }
+        }
+        row_group_sum<LPR, U, RPI>(S, red, it, slot, g);
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const double L = rho[u] * rho[u] * rho[u] * S[u] * p.inv_h;
+#pragma unroll
+            for (int v = 0; v < V; ++v) {
+                float xf[8], df[8], rf[8];
+                unpack8(xv[u][v], xf);
+                unpack8(dv[u][v], df);
+                if constexpr (DRES) unpack8(ld16(p.dres + off[u] + lv.col[v]), rf);
+                double d[8];
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    const double gw = w64[v][e] * (double)df[e];  // exact
+                    d[e] = __builtin_fma(gw, rho[u], -((double)xf[e] * L));
+                    if constexpr (DRES) d[e] += (double)rf[e];
+                }
+                uint4 o;
+                o.x = pack_bf16x2_from_f64(d[0], d[1]);
+                o.y = pack_bf16x2_from_f64(d[2], d[3]);
+                o.z = pack_bf16x2_from_f64(d[4], d[5]);
+                o.w = pack_bf16x2_from_f64(d[6], d[7]);
+                if (ok[u] && lv.ok[v]) st16_stream(p.dx + off[u] + lv.col[v], o);
+            }
+        }
+    }
+
+    // ---- chunk sum of dw ----------------------------------------------
+    if constexpr (SLOTS > 1) {
+#pragma unroll
+        for (int v = 0; v < V; ++v)
+            if (lv.ok[v]) {
+#pragma unroll
+                for (int e = 0; e < 8; ++e) slot_part[slot * H + lv.col[v] + e] = acc[v][e];
+            }
+        __syncthreads();
+        for (int col = tid; col < H; col += BLOCK) {
+            double s = slot_part[col];
+#pragma unroll
+            for (int sl = 1; sl < SLOTS; ++sl) s += slot_part[sl * H + col];
+            if (p.atomic_form) unsafeAtomicAdd(p.acc + col, s);
+            else p.part[(int64_t)chunk * H + col] = s;
+        }
+    } else {
+#pragma unroll
+        for (int v = 0; v < V; ++v)
+            if (lv.ok[v]) {
+                if (p.atomic_form) {
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) unsafeAtomicAdd(p.acc + lv.col[v] + e, acc[v][e]);
+                } else {
+                    double2* dst = reinterpret_cast<double2*>(p.part + (int64_t)chunk * H + lv.col[v]);
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) dst[e] = make_double2(acc[v][2 * e], acc[v][2 * e + 1]);
+                }
+            }
+    }
+
+    if (p.atomic_form) {
+        // Every workgroup publishes its atomics (agent-scope fence) before it
+        // takes a ticket; the one that draws the last ticket reads and clears
+        // the accumulator and writes dw.
+        __threadfence();
+        __syncthreads();
+        if (tid == 0) {
+            const unsigned t = __hip_atomic_fetch_add(p.ticket, 1u, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
+            last_block = (t == (unsigned)(gridDim.x - 1));
+        }
+        __syncthreads();
+        if (last_block) {
+            __threadfence();
+            for (int col = tid; col < H; col += BLOCK) {
+                unsigned long long* a = reinterpret_cast<unsigned long long*>(p.acc + col);
+                const unsigned long long bits =
+                    __hip_atomic_exchange(a, 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                p.dw[col] = (float)__longlong_as_double((long long)bits);
+            }
+            if (tid == 0) __hip_atomic_store(p.ticket, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
+    }
+}
+
+// ------------------------------------------------ fixed-order dw reduce ----
+// dw[col] = sum over chunks of part[chunk][col].  A workgroup takes 16
+// columns; its 16 lane groups q sum chunks q, q+16, q+32, ... in that order
+// (16 loads in flight per lane), and the 16 group sums are added in q order.
+// The order depends only on the chunk count.
+constexpr int kReduceCols = 16;
+constexpr int kReduceGroups = 16;
+
+__global__ void __launch_bounds__(kReduceCols * kReduceGroups)
+dw_reduce_kernel(const double* __restrict__ part, int chunks, int H, float* __restrict__ dw)
+{
+    constexpr int DEPTH = 16;
+    __shared__ double sums[kReduceGroups][kReduceCols];
+    const int c = threadIdx.x % kReduceCols;
+    const int q = threadIdx.x / kReduceCols;
+    const int col = blockIdx.x * kReduceCols + c;
+    double s = 0.0;
+    if (col < H) {
+        for (int k = q; k < chunks; k += DEPTH * kReduceGroups) {
+            double a[DEPTH];
+#pragma unroll
+            for (int i = 0; i < DEPTH; ++i) {
+                const int kk = k + i * kReduceGroups;
+                a[i] = kk < chunks ? part[(int64_t)kk * H + col] : 0.0;
+            }
+#pragma unroll
+            for (int i = 0; i < DEPTH; ++i) s += a[i];
+        }
+    }
+    sums[q][c] = s;
+    __syncthreads();
+    if (q == 0 && col < H) {
+        double t = sums[0][c];
+#pragma unroll
+        for (int j = 1; j < kReduceGroups; ++j) t += sums[j][c];
+        dw[col] = (float)t;
+    }
+}
+
+__global__ void fill_zero_kernel(uint32_t* p, int64_t words)
+{
+    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < words;
+         i += (int64_t)gridDim.x * blockDim.x)
+        p[i] = 0u;
+}
+
+// ----------------------------------------------------------- launchers ----
+
+template <int LPR, int V, int U, bool WF32, bool DRES>
+static hipError_t bwd_t(const BwdParams& p, hipStream_t s)
+{
+    constexpr int SLOTS = slots_of(LPR);
+    const size_t lds = SLOTS > 1 ? (size_t)SLOTS * p.H * sizeof(double) : 0;
+    if (lds > (size_t)kMaxSlotLds) return hipErrorInvalidConfiguration;
+    hipLaunchKernelGGL((bwd_kernel<LPR, V, U, WF32, DRES>), dim3(p.chunks), dim3(block_of(LPR)), lds, s, p);
+    return hipGetLastError();
+}
+
+template <int LPR, int V, int U>
+static hipError_t bwd_dispatch(bool w_f32, const BwdParams& p, hipStream_t s)
+{
+    if (p.dres) return w_f32 ? bwd_t<LPR, V, U, true, true>(p, s) : bwd_t<LPR, V, U, false, true>(p, s);
+    return w_f32 ? bwd_t<LPR, V, U, true, false>(p, s) : bwd_t<LPR, V, U, false, false>(p, s);
+}
+
+hipError_t launch_bwd(int layout, bool w_f32, const BwdParams& p, hipStream_t s)
+{
+    switch (layout) {
+#define RMSN_BWD_CASE(id, mh, l, vv, uu) \
+    case id: return bwd_dispatch<l, vv, uu>(w_f32, p, s);
+        RMSN_BWD_LAYOUTS(RMSN_BWD_CASE)
+#undef RMSN_BWD_CASE
+    default: return hipErrorInvalidValue;
+    }
+}
+
+hipError_t launch_dw_reduce(const double* part, int chunks, int H, float* dw, hipStream_t s)
+{
+    const int grid = (H + kReduceCols - 1) / kReduceCols;
+    hipLaunchKernelGGL(dw_reduce_kernel, dim3(grid), dim3(kReduceCols * kReduceGroups), 0, s, part, chunks, H, dw);
+    return hipGetLastError();
+}
+
+hipError_t launch_fill_zero(void* ptr, int64_t bytes, hipStream_t s)
+{
+    const int64_t words = bytes / 4;
+    if (words <= 0) return hipSuccess;
+    int64_t blocks = (words + 255) / 256;
+    if (blocks > 1024) blocks = 1024;
+    hipLaunchKernelGGL(fill_zero_kernel, dim3((int)blocks), dim3(256), 0, s, static_cast<uint32_t*>(ptr), words);
+    return hipGetLastError();
+}
+
+}  // namespace rmsn

@@ -33,7 +33,7 @@ struct BwdParams {
     unsigned* ticket;     // arrival counter (atomic form), zero on entry and exit
     int64_t stride_t, stride_h;
     int R, heads, H;
-    int rows_per_chunk, chunks;
+    int chunks;           // workgroups; workgroup c takes row groups c, c + chunks, ...
     int atomic_form;
     double inv_h;
 };

@@ -23,26 +23,30 @@ struct Layout {
     int u;      // rows per row group per iteration
 };
 
-// X(id, max_h, lpr, v, u)
+// X(id, max_h, lpr, v, u); max_h == lpr * v * 8.  A tuning build may supply
+// its own candidate tables through RMSN_LAYOUTS_OVERRIDE.
+#ifdef RMSN_LAYOUTS_OVERRIDE
+#include RMSN_LAYOUTS_OVERRIDE
+#else
 #define RMSN_FWD_LAYOUTS(X) \
     X(0, 64, 8, 1, 4)       \
     X(1, 128, 16, 1, 4)     \
-    X(2, 256, 32, 1, 4)     \
+    X(2, 256, 16, 2, 4)     \
     X(3, 512, 64, 1, 2)     \
     X(4, 1024, 64, 2, 2)    \
-    X(5, 1536, 64, 3, 1)    \
+    X(5, 1536, 32, 6, 1)    \
     X(6, 2048, 64, 4, 1)    \
     X(7, 3072, 64, 6, 1)    \
-    X(8, 4096, 64, 8, 1)    \
-    X(9, 5120, 64, 10, 1)   \
-    X(10, 6144, 64, 12, 1)  \
+    X(8, 4096, 256, 2, 2)   \
+    X(9, 5120, 128, 5, 1)   \
+    X(10, 6144, 768, 1, 2)  \
     X(11, 8192, 128, 8, 1)  \
     X(12, 16384, 256, 8, 1)
 
 #define RMSN_BWD_LAYOUTS(X) \
     X(0, 64, 8, 1, 2)       \
     X(1, 128, 16, 1, 2)     \
-    X(2, 256, 32, 1, 2)     \
+    X(2, 256, 8, 4, 1)      \
     X(3, 512, 64, 1, 2)     \
     X(4, 1024, 64, 2, 1)    \
     X(5, 1536, 64, 3, 1)    \
@@ -51,6 +55,21 @@ struct Layout {
     X(8, 6144, 256, 3, 1)   \
     X(9, 8192, 512, 2, 1)   \
     X(10, 16384, 1024, 2, 1)
+#endif
+
+#define RMSN_CHECK_LAYOUT(id, mh, l, vv, uu) static_assert((mh) == (l) * (vv) * 8, "layout width");
+RMSN_FWD_LAYOUTS(RMSN_CHECK_LAYOUT)
+RMSN_BWD_LAYOUTS(RMSN_CHECK_LAYOUT)
+#undef RMSN_CHECK_LAYOUT
+
+// The backward combines its row groups' FP64 column sums in LDS:
+// SLOTS * H * 8 bytes, which must stay within kMaxSlotLds.
+constexpr long kMaxSlotLds = 64 * 1024;
+#define RMSN_CHECK_LDS(id, mh, l, vv, uu)                                                       \
+    static_assert((l) >= 256 || (256 / (l)) == 1 || (long)(256 / (l)) * (mh) * 8 <= kMaxSlotLds, \
+                  "backward layout needs too much LDS");
+RMSN_BWD_LAYOUTS(RMSN_CHECK_LDS)
+#undef RMSN_CHECK_LDS
 
 #define RMSN_LAYOUT_ENTRY(id, mh, l, vv, uu) Layout{mh, l, vv, uu},
 static constexpr Layout kFwdLayouts[] = {RMSN_FWD_LAYOUTS(RMSN_LAYOUT_ENTRY)};
@@ -60,7 +79,9 @@ static constexpr Layout kBwdLayouts[] = {RMSN_BWD_LAYOUTS(RMSN_LAYOUT_ENTRY)};
 static constexpr int kNumFwdLayouts = sizeof(kFwdLayouts) / sizeof(kFwdLayouts[0]);
 static constexpr int kNumBwdLayouts = sizeof(kBwdLayouts) / sizeof(kBwdLayouts[0]);
 
-constexpr int block_of(int lpr) { return lpr > 256 ? lpr : 256; }
+// Workgroup size: the largest multiple of LPR not above 256, or LPR itself
+// when a row spans more than 256 lanes.
+constexpr int block_of(int lpr) { return lpr >= 256 ? lpr : lpr * (256 / lpr); }
 constexpr int slots_of(int lpr) { return block_of(lpr) / lpr; }
 
 // Smallest layout that covers H (tables are sorted by max_h); -1 if none.

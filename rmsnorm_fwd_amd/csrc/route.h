@@ -12,8 +12,8 @@ namespace rmsn {
 enum { FORM_PAIR = 0, FORM_ATOMIC = 1 };
 
 struct BwdRoute {
-    int form;            // FORM_PAIR or FORM_ATOMIC
-    int rows_per_chunk;  // rows per workgroup of the backward row kernel
+    int form;    // FORM_PAIR or FORM_ATOMIC
+    int chunks;  // workgroups of the row kernel (= FP64 partial rows of the pair form)
 };
 
 // Workspace layout: [0, 256) header (arrival ticket at offset 0),
@@ -23,10 +23,6 @@ constexpr size_t kWsHeader = 256;
 inline size_t pad256(size_t b) { return (b + 255) & ~(size_t)255; }
 inline size_t ws_acc_offset() { return kWsHeader; }
 inline size_t ws_part_offset(int64_t H) { return kWsHeader + pad256((size_t)H * 8); }
-inline int64_t chunks_of(int64_t R, int64_t rows_per_chunk)
-{
-    return rows_per_chunk > 0 ? (R + rows_per_chunk - 1) / rows_per_chunk : 0;
-}
 size_t ws_bytes_for(int64_t R, int64_t H, const BwdRoute& r);
 
 // The measured route table (route.cpp).
@@ -36,6 +32,6 @@ BwdRoute default_bwd_route(int64_t R, int64_t H, bool w_f32, bool residual, bool
 int bwd_rows_per_iter(int64_t H);
 
 // Largest chunk count a route may ask for.
-constexpr int64_t kMaxChunks = 1 << 20;
+constexpr int64_t kMaxChunks = 1 << 16;
 
 }  // namespace rmsn

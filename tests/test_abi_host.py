@@ -125,7 +125,7 @@ def test_workspace_size_is_pure_and_covers_both_modes():
     assert rn.rmsnorm_bwd_workspace_size(-1, 1, 64, True) == 0
 
 
-def test_route_rows_per_chunk_depend_only_on_shape():
+def test_route_chunks_depend_only_on_shape():
     # deterministic dw is fixed by the chunking; it must not vary with anything
     # but the shape (and never with the device's compute-unit count).
     r1 = rn.rmsnorm_bwd_route(65536, 1, 4096, 1, 0, 1)

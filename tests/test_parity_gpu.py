@@ -76,3 +76,19 @@ def test_zero_rows_backward_writes_zero_dw():
     dx, dw = rn.rmsnorm_bwd(x, x, rstd, w, dw=dw)
     torch.cuda.synchronize()
     assert y.numel() == 0 and int(dw.count_nonzero()) == 0
+
+
+@pytest.mark.parametrize("H", [256, 1536, 4096, 6144])
+def test_routes_agree(H):
+    # both sides of every route choice: pair and atomic forms at several
+    # chunk counts (including more chunks than row groups); dx must be
+    # bitwise the same for all of them and dw within budget for each
+    routes = [(0, 1), (0, 7), (0, 512), (0, 1000), (1, 1), (1, 5), (1, 256)]
+    rep = run_case(Layout.plain(333, H), "bf16", seed=21, routes=routes)
+    print(H, rep)
+
+
+def test_deterministic_dw_repeats_at_scale():
+    # ten repeats of the deterministic backward on a large case
+    rep = run_case(Layout.plain(16384, 4096), "f32", seed=2, det_repeats=10)
+    print(rep)
