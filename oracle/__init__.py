@@ -56,6 +56,8 @@ def _load():
     lib.oracle_bwd_bf16.argtypes = [_i64, _i64, _ptr, _ptr, _ptr, ctypes.c_int, _ptr,
                                     _ptr, _ptr, _ptr, _ptr]
     lib.oracle_bwd_bf16.restype = ctypes.c_int
+    lib.oracle_dw_bf16.argtypes = [_i64, _i64, _ptr, _ptr, _ptr, _ptr]
+    lib.oracle_dw_bf16.restype = None
     lib.oracle_num_threads.argtypes = []
     lib.oracle_num_threads.restype = ctypes.c_int
     _lib = lib
@@ -177,3 +179,14 @@ def bwd_bf16(u: np.ndarray, dy: np.ndarray, w: np.ndarray, rho32: np.ndarray,
     if rc != 0:
         raise RuntimeError(f"oracle_bwd_bf16 failed ({rc})")
     return dx, dx64, dw
+
+
+def dw_bf16(u: np.ndarray, dy: np.ndarray, rho32: np.ndarray) -> np.ndarray:
+    """dw alone (FP64) from BF16 rows at the kernel's FP32 rstd."""
+    u = _c(u, np.uint16)
+    dy = _c(dy, np.uint16)
+    rho32 = _c(rho32, np.float32)
+    R, H = u.shape
+    dw = np.empty(H, dtype=np.float64)
+    _load().oracle_dw_bf16(R, H, _p(u), _p(dy), _p(rho32), _p(dw))
+    return dw

@@ -277,6 +277,27 @@ int oracle_bwd_bf16(int64_t R, int64_t H, const uint16_t* u16, const uint16_t* d
     return failed ? 2 : 0;
 }
 
+/* dw alone: dw[j] = sum over rows of dy[r,j] * (u[r,j] * rho[r]), each
+ * column summed over the rows in row order -- the same sum as the dw of
+ * oracle_bwd_bf16, for full-size checks that do not need dx. */
+void oracle_dw_bf16(int64_t R, int64_t H, const uint16_t* u16, const uint16_t* dy16,
+                    const float* rho32, double* dw)
+{
+#pragma omp parallel for schedule(static)
+    for (int64_t j0 = 0; j0 < H; j0 += 64) {
+        int64_t j1 = j0 + 64 < H ? j0 + 64 : H;
+        double acc[64];
+        for (int64_t j = j0; j < j1; ++j) acc[j - j0] = 0.0;
+        for (int64_t row = 0; row < R; ++row) {
+            const double rho = (double)rho32[row];
+            for (int64_t j = j0; j < j1; ++j)
+                acc[j - j0] += oracle_bf16_to_double(dy16[row * H + j]) *
+                               (oracle_bf16_to_double(u16[row * H + j]) * rho);
+        }
+        for (int64_t j = j0; j < j1; ++j) dw[j] = acc[j - j0];
+    }
+}
+
 int oracle_num_threads(void)
 {
     int n = 1;

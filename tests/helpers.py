@@ -111,8 +111,9 @@ class Layout:
         return buf
 
     def empty(self, device="cuda"):
-        return self.place(np.zeros((0, self.H), np.uint16), device) if self.R == 0 else \
-            self.place(np.full((self.R, self.H), SENTINEL, np.uint16), device)
+        """Device buffer for an output, every element set to the sentinel."""
+        t = torch()
+        return t.full((self.buffer_elems(),), SENTINEL, dtype=t.int16, device=device).view(t.bfloat16)
 
     def rows_of(self, buf) -> np.ndarray:
         if self.R == 0:
@@ -256,4 +257,74 @@ def run_case(L: Layout, wdt: str = "bf16", res: bool = False, dres: bool = False
     # the atomic form leaves its accumulator and ticket at zero
     acc_bytes = 256 + ((L.H * 8 + 255) // 256) * 256
     assert int(ws[:acc_bytes].count_nonzero()) == 0, "non-deterministic workspace not left clean"
+    return rep
+
+
+def run_full(L: Layout, wdt: str = "bf16", res: bool = False, dres: bool = False, seed: int = 0,
+             family: str = "normal", n_sample: int = 384, det_repeats: int = 3) -> Report:
+    """Full-size case: the whole forward and backward run on the GPU; y, h,
+    rstd and dx are compared with the oracle on sampled rows (first, last,
+    middle and random rows), dw with the oracle's full column sums, dx between
+    modes and the deterministic dw across repeats bit for bit on the device."""
+    import rmsnorm_fwd_amd as rn
+    t = torch()
+    rep = Report()
+    R, H = L.R, L.H
+    x, r, dy, dr, w = gen_case(seed, L, wdt, res, dres, family)
+    xb = L.place(x)
+    rb = L.place(r) if res else None
+    dyb = L.place(dy)
+    drb = L.place(dr) if dres else None
+    wd = weight_dev(w)
+
+    def fwd(det):
+        yb = L.empty()
+        hb = L.empty() if res else None
+        rstd = t.empty(R, dtype=t.float32, device="cuda")
+        rn.rmsnorm_fwd(L.view(xb), wd, EPS, residual=L.view(rb) if res else None, deterministic=det,
+                       y=L.view(yb), residual_out=L.view(hb) if res else None, rstd=rstd)
+        return yb, hb, rstd
+
+    yb, hb, rstd = fwd(True)
+    rng = np.random.default_rng(1000 + seed)
+    rows = np.unique(np.concatenate([[0, 1, R // 2, R - 2, R - 1], rng.integers(0, R, n_sample)]))
+    rows = rows[(rows >= 0) & (rows < R)]
+    idx = t.from_numpy(rows).to("cuda")
+
+    def sampled(buf):
+        return to_host_bits(L.view(buf).reshape(R, H).index_select(0, idx))
+
+    rstd_h = rstd.cpu().numpy()
+    ref_y, ref_h, ref_rstd = oracle.fwd_bf16(x[rows], w, EPS, r[rows] if res else None)
+    check_fwd(sampled(yb), sampled(hb) if res else None, rstd_h[rows], ref_y, ref_h, ref_rstd, rep)
+    yb2, hb2, rstd2 = fwd(False)
+    assert t.equal(L.view(yb2), L.view(yb)) and t.equal(rstd2, rstd), "forward not bitwise repeatable"
+    if res:
+        assert t.equal(L.view(hb2), L.view(hb))
+    del yb2, hb2, rstd2
+
+    ub = hb if res else xb
+    u_rows = ref_h if res else x[rows]
+    ref_dx, _, _ = oracle.bwd_bf16(u_rows, dy[rows], w, rstd_h[rows], dr[rows] if dres else None)
+    u_full = oracle.residual_add(x, r) if res else x
+    ref_dw = oracle.dw_bf16(u_full, dy, rstd_h)
+    ws = rn.rmsnorm_bwd_workspace(L.T, L.heads, L.H, "cuda")
+
+    def bwd(det):
+        dxb = L.empty()
+        dw = t.empty(H, dtype=t.float32, device="cuda")
+        rn.rmsnorm_bwd(L.view(dyb), L.view(ub), rstd, wd, residual=L.view(drb) if dres else None,
+                       deterministic=det, dx=L.view(dxb), dw=dw, workspace=ws)
+        return dxb, dw
+
+    dx_det, dw_det = bwd(True)
+    check_dx(sampled(dx_det), ref_dx, rep)
+    check_dw(dw_det.cpu().numpy(), ref_dw, rep)
+    for _ in range(det_repeats):
+        dxb, dw = bwd(True)
+        assert t.equal(dw, dw_det), "deterministic dw not reproducible"
+        del dxb
+    dx_nd, dw_nd = bwd(False)
+    assert t.equal(L.view(dx_nd), L.view(dx_det)), "dx differs between modes"
+    check_dw(dw_nd.cpu().numpy(), ref_dw, rep)
     return rep

@@ -304,3 +304,12 @@ def test_bf16_path_against_torch_fp64(wdt, res):
     # and against autograd at the FP64 rstd (differs only through rho32)
     (ty * torch.from_numpy(oracle.bf16_to_f64(dy))).sum().backward()
     np.testing.assert_allclose(dw, tw.grad.numpy(), rtol=1e-6, atol=1e-6)
+
+
+def test_dw_alone_equals_backward_dw():
+    R, H = 300, 200
+    u = synth.rows(4, "x", 0, R, H)
+    dy = synth.rows(4, "dy", 0, R, H)
+    rho = np.random.default_rng(6).uniform(0.5, 2.0, R).astype(np.float32)
+    _, _, dw = oracle.bwd_bf16(u, dy, synth.weight(4, H, "bf16"), rho)
+    assert np.array_equal(oracle.dw_bf16(u, dy, rho), dw)
