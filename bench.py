@@ -263,16 +263,17 @@ def main():
     import rmsnorm_fwd_amd as rn
 
     rn.lib()  # fail loudly if the HIP library is not built
-    wl = Workload(args.workload)
-    log(f"workload {wl.name}: R={wl.R} H={wl.H} w={wl.wdt} res={wl.res}")
-
     if args.copy_calibration:
+        # the first three device-to-device copies of the process: 1 GiB each
         src = torch.empty(1 << 29, dtype=torch.int16, device="cuda").fill_(3)
         dst = torch.empty_like(src)
         for _ in range(3):
             dst.copy_(src)
         torch.cuda.synchronize()
+        del src, dst
         log("copy calibration: 3 x copy of 1 GiB done")
+    wl = Workload(args.workload)
+    log(f"workload {wl.name}: R={wl.R} H={wl.H} w={wl.wdt} res={wl.res}")
 
     # warmup + timed steps (deterministic backward), back to back
     for _ in range(args.warmup):

@@ -143,7 +143,7 @@ int rmsnorm_fwd(const void* x, const void* residual, const void* w, int w_dtype,
     const Layout& L = kFwdLayouts[layout];
     const int64_t rpi = (int64_t)slots_of(L.lpr) * L.u;
     const int64_t iters = (s.R + rpi - 1) / rpi;
-    const int64_t cap = (int64_t)cu_count() * 16;  // measured: 16 per CU best or tied at T >= 65536
+    const int64_t cap = (int64_t)cu_count() * L.k;
     const int grid = (int)(iters < cap ? iters : cap);
 
     FwdParams p{};

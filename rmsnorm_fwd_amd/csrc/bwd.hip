@@ -285,7 +285,7 @@ static hipError_t bwd_dispatch(bool w_f32, const BwdParams& p, hipStream_t s)
 hipError_t launch_bwd(int layout, bool w_f32, const BwdParams& p, hipStream_t s)
 {
     switch (layout) {
-#define RMSN_BWD_CASE(id, mh, l, vv, uu) \
+#define RMSN_BWD_CASE(id, mh, l, vv, uu, kk) \
     case id: return bwd_dispatch<l, vv, uu>(w_f32, p, s);
         RMSN_BWD_LAYOUTS(RMSN_BWD_CASE)
 #undef RMSN_BWD_CASE

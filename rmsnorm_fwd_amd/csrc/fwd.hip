@@ -156,7 +156,7 @@ static hipError_t fwd_dispatch(bool w_f32, const FwdParams& p, int grid, hipStre
 hipError_t launch_fwd(int layout, bool w_f32, const FwdParams& p, int grid, hipStream_t s)
 {
     switch (layout) {
-#define RMSN_FWD_CASE(id, mh, l, vv, uu) \
+#define RMSN_FWD_CASE(id, mh, l, vv, uu, kk) \
     case id: return fwd_dispatch<l, vv, uu>(w_f32, p, grid, s);
         RMSN_FWD_LAYOUTS(RMSN_FWD_CASE)
 #undef RMSN_FWD_CASE

@@ -21,43 +21,48 @@ struct Layout {
     int lpr;    // lanes per row
     int v;      // 16-byte vectors per lane per row
     int u;      // rows per row group per iteration
+    int k;      // forward: workgroups per compute unit (grid cap);
+                // backward: workgroups ("chunks") of the row kernel
 };
 
-// X(id, max_h, lpr, v, u); max_h == lpr * v * 8.  A tuning build may supply
-// its own candidate tables through RMSN_LAYOUTS_OVERRIDE.
+// X(id, max_h, lpr, v, u, k); max_h == lpr * v * 8.  Every entry was picked
+// by timing the candidates on MI355X with cold caches (T*H between 2^25 and
+// 2^30 elements); the smallest max_h >= H serves H.  A tuning build may
+// supply its own candidate tables through RMSN_LAYOUTS_OVERRIDE.
 #ifdef RMSN_LAYOUTS_OVERRIDE
 #include RMSN_LAYOUTS_OVERRIDE
 #else
-#define RMSN_FWD_LAYOUTS(X) \
-    X(0, 64, 8, 1, 4)       \
-    X(1, 128, 16, 1, 4)     \
-    X(2, 256, 16, 2, 4)     \
-    X(3, 512, 64, 1, 2)     \
-    X(4, 1024, 64, 2, 2)    \
-    X(5, 1536, 32, 6, 1)    \
-    X(6, 2048, 64, 4, 1)    \
-    X(7, 3072, 64, 6, 1)    \
-    X(8, 4096, 256, 2, 2)   \
-    X(9, 5120, 128, 5, 1)   \
-    X(10, 6144, 768, 1, 2)  \
-    X(11, 8192, 128, 8, 1)  \
-    X(12, 16384, 256, 8, 1)
+#define RMSN_FWD_LAYOUTS(X)    \
+    X(0, 64, 8, 1, 4, 64)      \
+    X(1, 128, 16, 1, 4, 64)    \
+    X(2, 256, 16, 2, 2, 64)    \
+    X(3, 512, 32, 2, 2, 64)    \
+    X(4, 1024, 32, 4, 1, 64)   \
+    X(5, 1536, 32, 6, 1, 16)   \
+    X(6, 2048, 32, 8, 1, 32)   \
+    X(7, 3072, 64, 6, 1, 32)   \
+    X(8, 4096, 256, 2, 2, 16)  \
+    X(9, 5120, 128, 5, 1, 16)  \
+    X(10, 6144, 768, 1, 2, 16) \
+    X(11, 8192, 512, 2, 2, 32) \
+    X(12, 16384, 512, 4, 1, 8)
 
-#define RMSN_BWD_LAYOUTS(X) \
-    X(0, 64, 8, 1, 2)       \
-    X(1, 128, 16, 1, 2)     \
-    X(2, 256, 8, 4, 1)      \
-    X(3, 512, 64, 1, 2)     \
-    X(4, 1024, 64, 2, 1)    \
-    X(5, 1536, 64, 3, 1)    \
-    X(6, 2048, 256, 1, 1)   \
-    X(7, 4096, 256, 2, 1)   \
-    X(8, 6144, 256, 3, 1)   \
-    X(9, 8192, 512, 2, 1)   \
-    X(10, 16384, 1024, 2, 1)
+#define RMSN_BWD_LAYOUTS(X)       \
+    X(0, 64, 8, 1, 2, 512)        \
+    X(1, 128, 16, 1, 2, 512)      \
+    X(2, 256, 16, 2, 2, 512)      \
+    X(3, 512, 32, 2, 2, 512)      \
+    X(4, 1024, 64, 2, 1, 512)     \
+    X(5, 1536, 64, 3, 1, 512)     \
+    X(6, 2048, 128, 2, 1, 512)    \
+    X(7, 3072, 128, 3, 1, 512)    \
+    X(8, 4096, 256, 2, 1, 512)    \
+    X(9, 6144, 256, 3, 1, 512)    \
+    X(10, 8192, 1024, 1, 1, 256)  \
+    X(11, 16384, 512, 4, 1, 256)
 #endif
 
-#define RMSN_CHECK_LAYOUT(id, mh, l, vv, uu) static_assert((mh) == (l) * (vv) * 8, "layout width");
+#define RMSN_CHECK_LAYOUT(id, mh, l, vv, uu, kk) static_assert((mh) == (l) * (vv) * 8, "layout width");
 RMSN_FWD_LAYOUTS(RMSN_CHECK_LAYOUT)
 RMSN_BWD_LAYOUTS(RMSN_CHECK_LAYOUT)
 #undef RMSN_CHECK_LAYOUT
@@ -65,13 +70,13 @@ RMSN_BWD_LAYOUTS(RMSN_CHECK_LAYOUT)
 // The backward combines its row groups' FP64 column sums in LDS:
 // SLOTS * H * 8 bytes, which must stay within kMaxSlotLds.
 constexpr long kMaxSlotLds = 64 * 1024;
-#define RMSN_CHECK_LDS(id, mh, l, vv, uu)                                                       \
+#define RMSN_CHECK_LDS(id, mh, l, vv, uu, kk)                                                   \
     static_assert((l) >= 256 || (256 / (l)) == 1 || (long)(256 / (l)) * (mh) * 8 <= kMaxSlotLds, \
                   "backward layout needs too much LDS");
 RMSN_BWD_LAYOUTS(RMSN_CHECK_LDS)
 #undef RMSN_CHECK_LDS
 
-#define RMSN_LAYOUT_ENTRY(id, mh, l, vv, uu) Layout{mh, l, vv, uu},
+#define RMSN_LAYOUT_ENTRY(id, mh, l, vv, uu, kk) Layout{mh, l, vv, uu, kk},
 static constexpr Layout kFwdLayouts[] = {RMSN_FWD_LAYOUTS(RMSN_LAYOUT_ENTRY)};
 static constexpr Layout kBwdLayouts[] = {RMSN_BWD_LAYOUTS(RMSN_LAYOUT_ENTRY)};
 #undef RMSN_LAYOUT_ENTRY

@@ -32,15 +32,19 @@ BwdRoute default_bwd_route(int64_t R, int64_t H, bool w_f32, bool residual, bool
     (void)w_f32;
     (void)residual;
     (void)deterministic;
-    const int64_t rpi = bwd_rows_per_iter(H);
+    const int id = pick_layout(kBwdLayouts, kNumBwdLayouts, H);
+    const Layout& L = kBwdLayouts[id < 0 ? 0 : id];
+    const int64_t rpi = (int64_t)slots_of(L.lpr) * L.u;
     const int64_t groups = (R + rpi - 1) / rpi;
     BwdRoute r;
-    // Measured on MI355X (T 65536, H 1536 to 6144, both weight dtypes):
-    // 512 workgroups -- two per compute unit -- beat 256, 768, 1024 and more
-    // by 4-20 %, and the fixed-order pair beats the atomic form by 25-50 %,
-    // so both modes take the pair at these sizes.
+    // Measured on MI355X with cold caches, T*H from 2^23 to 2^30 elements,
+    // both weight dtypes: the layout's chunk count (512 -- two workgroups per
+    // compute unit -- for H <= 6144, 256 above) beats the other counts by
+    // 4-20 %, and the fixed-order pair beats the atomic form at every shape
+    // (FP64 atomics from hundreds of workgroups to the same H addresses
+    // serialise), so both modes take the pair.
     r.form = FORM_PAIR;
-    r.chunks = (int)(groups < 512 ? (groups > 0 ? groups : 1) : 512);
+    r.chunks = (int)(groups < L.k ? (groups > 0 ? groups : 1) : L.k);
     return r;
 }
 
