@@ -1,0 +1,86 @@
+"""torch.autograd wrapper over the C-ABI forward and backward.
+
+The pages expose the training RMSNorm to autograd through a Function class
+and a functional entry point, both taking ``deterministic`` (p1 #8208 PR
+description: cake_rmsnorm, CakeRMSNormFunction).  Their measured op
+"2xfwd+bwd" is the checkpointed step -- forward, forward recompute,
+backward (p2 "Key") -- which ``recompute=True`` gives here: the forward keeps
+only its inputs and the backward runs the forward again before the backward
+kernel.
+
+Gradient dtypes follow autograd's rule (a gradient has its tensor's dtype):
+the weight gradient is the library's FP32 dw, cast to w's dtype when w is
+BF16.  Call ``rmsnorm_bwd`` directly to keep the FP32 dw.
+"""
+from __future__ import annotations
+
+import torch
+
+from . import geometry, rmsnorm_bwd, rmsnorm_fwd
+
+
+def _like_layout(t, ref):
+    """t with ref's shape and strides (the ABI shares strides between all
+    activation tensors); copies only when the layouts differ."""
+    if t is None:
+        return None
+    if t.dtype == torch.bfloat16 and t.shape == ref.shape and geometry(t) == geometry(ref):
+        return t
+    out = torch.empty_strided(ref.shape, ref.stride(), dtype=torch.bfloat16, device=ref.device)
+    out.copy_(t)
+    return out
+
+
+class RMSNormFunction(torch.autograd.Function):
+    """y = RMSNorm(x [+ residual]) * w.  Returns y, or (y, h) with a residual,
+    where h = x + residual is the BF16 residual stream."""
+
+    @staticmethod
+    def forward(ctx, x, w, residual, eps, deterministic, recompute):
+        ctx.set_materialize_grads(False)
+        y, rstd, h = rmsnorm_fwd(x, w, eps, residual=residual, deterministic=deterministic)
+        ctx.eps, ctx.deterministic, ctx.recompute = eps, deterministic, recompute
+        ctx.has_residual = residual is not None
+        if recompute:
+            ctx.save_for_backward(x, w, residual)
+        else:
+            ctx.save_for_backward(h if residual is not None else x, w, rstd)
+        if residual is not None:
+            return y, h
+        return y
+
+    @staticmethod
+    def backward(ctx, dy, dh=None):
+        if ctx.recompute:
+            x, w, residual = ctx.saved_tensors
+            _, rstd, h = rmsnorm_fwd(x, w, ctx.eps, residual=residual, deterministic=ctx.deterministic)
+            u = h if residual is not None else x
+        else:
+            u, w, rstd = ctx.saved_tensors
+        if dy is None:  # only h was used downstream
+            dy = torch.zeros_like(u)
+        dy = _like_layout(dy, u)
+        dres = _like_layout(dh, u) if ctx.has_residual and dh is not None else None
+        dx, dw = rmsnorm_bwd(dy, u, rstd, w, residual=dres, deterministic=ctx.deterministic)
+        grad_w = dw if w.dtype == torch.float32 else dw.to(w.dtype)
+        grad_res = dx if ctx.has_residual else None
+        return dx, grad_w, grad_res, None, None, None
+
+
+def rmsnorm(x, w, eps: float = 1e-6, residual=None, deterministic: bool = True,
+            recompute: bool = False):
+    """Functional form of :class:`RMSNormFunction`."""
+    return RMSNormFunction.apply(x, w, residual, eps, deterministic, recompute)
+
+
+class RMSNorm(torch.nn.Module):
+    """Module holding the weight (BF16 or FP32, initialised to ones)."""
+
+    def __init__(self, hidden: int, eps: float = 1e-6, dtype=torch.bfloat16, device=None,
+                 deterministic: bool = True, recompute: bool = False):
+        super().__init__()
+        self.weight = torch.nn.Parameter(torch.ones(hidden, dtype=dtype, device=device))
+        self.eps, self.deterministic, self.recompute = eps, deterministic, recompute
+
+    def forward(self, x, residual=None):
+        return rmsnorm(x, self.weight, self.eps, residual, self.deterministic, self.recompute)
