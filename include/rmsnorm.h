@@ -141,9 +141,11 @@ int rmsnorm_bwd(const void* dy, const void* x, const float* rstd, const void* w,
  * backward reduces dw over rows:
  *   form   RMSN_FORM_PAIR: each of `chunks` workgroups writes an FP64 column
  *          partial to the workspace and a second kernel sums them in a fixed
- *          order (deterministic); RMSN_FORM_ATOMIC: the workgroups add their
- *          partials to an FP64 accumulator atomically and the last one to
- *          finish writes dw (one launch; order of additions not fixed).
+ *          order (deterministic; with chunks = 1 the one workgroup writes dw
+ *          itself and there is no second kernel); RMSN_FORM_ATOMIC: the
+ *          workgroups add their partials to an FP64 accumulator atomically
+ *          and the last one to finish writes dw (one launch; order of
+ *          additions not fixed).
  *   chunks number of workgroups of the row kernel, 1 .. 65536; workgroup c
  *          takes the row groups c, c + chunks, c + 2*chunks, ...
  * The per-row work, and so dx, does not depend on the route.

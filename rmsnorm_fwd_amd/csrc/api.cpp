@@ -94,11 +94,12 @@ int bwd_impl(const void* dy, const void* x, const float* rstd, const void* w, in
     p.heads = (int)s.heads;
     p.H = (int)s.H;
     p.chunks = r.chunks;
-    p.atomic_form = r.form == FORM_ATOMIC;
+    p.form = r.form;
+    p.direct_dw = r.form == FORM_PAIR && r.chunks == 1;
     p.inv_h = 1.0 / (double)s.H;
     hipError_t e = launch_bwd(layout, w_dtype == RMSN_W_F32, p, stream);
     if (e != hipSuccess) return RMSN_ERR_HIP;
-    if (r.form == FORM_PAIR) e = launch_dw_reduce(p.part, p.chunks, p.H, dw, stream);
+    if (r.form == FORM_PAIR && !p.direct_dw) e = launch_dw_reduce(p.part, p.chunks, p.H, dw, stream);
     return status_of(e);
 }
 

@@ -19,8 +19,8 @@
 // lane does not own).
 //
 // dw.  Each lane keeps FP64 column sums over the chunk's rows in registers;
-// row groups of one workgroup are added in LDS in slot order.  The chunk sum
-// then goes
+// row groups of one workgroup are added in LDS in slot order.  With a single
+// chunk that sum is dw and is written directly; otherwise the chunk sum goes
 //   pair form:   to row `chunk` of a workspace [chunks, H] (FP64), summed by
 //                dw_reduce_kernel in a fixed order -- deterministic;
 //   atomic form: into an FP64 [H] accumulator by atomic add; the workgroup
@@ -28,9 +28,35 @@
 //                accumulator and ticket -- one launch, no waiting.
 #include "device_common.h"
 #include "kernels.h"
+#include "route.h"
 
 
 namespace rmsn {
+
+// ------------------------------------------------ fixed-order dw reduce ----
+// dw[col] = sum over chunks of part[chunk][col], in one fixed order: lane
+// group q (of 16) sums chunks q, q+16, q+32, ... in that order, 16 loads in
+// flight (missing chunks add +0.0), and the 16 group sums are added in q
+// order.  The order depends only on the chunk count.
+constexpr int kReduceCols = 16;
+constexpr int kReduceGroups = 16;
+
+__device__ __forceinline__ double chunk_group_sum(const double* part, int chunks, int H, int col, int q)
+{
+    constexpr int DEPTH = 16;
+    double s = 0.0;
+    for (int k = q; k < chunks; k += DEPTH * kReduceGroups) {
+        double a[DEPTH];
+#pragma unroll
+        for (int i = 0; i < DEPTH; ++i) {
+            const int kk = k + i * kReduceGroups;
+            a[i] = kk < chunks ? part[(int64_t)kk * H + col] : 0.0;
+        }
+#pragma unroll
+        for (int i = 0; i < DEPTH; ++i) s += a[i];
+    }
+    return s;
+}
 
 // One iteration's rows of a row group: addresses, rstd and the x / dy vectors.
 template <int U, int V>
@@ -175,16 +201,20 @@ __global__ void __launch_bounds__(block_of(LPR)) bwd_kernel(BwdParams p)
             double s = slot_part[col];
 #pragma unroll
             for (int sl = 1; sl < SLOTS; ++sl) s += slot_part[sl * H + col];
-            if (p.atomic_form) unsafeAtomicAdd(p.acc + col, s);
+            if (p.form == FORM_ATOMIC) unsafeAtomicAdd(p.acc + col, s);
+            else if (p.direct_dw) p.dw[col] = (float)s;
             else p.part[(int64_t)chunk * H + col] = s;
         }
     } else {
 #pragma unroll
         for (int v = 0; v < V; ++v)
             if (lv.ok[v]) {
-                if (p.atomic_form) {
+                if (p.form == FORM_ATOMIC) {
 #pragma unroll
                     for (int e = 0; e < 8; ++e) unsafeAtomicAdd(p.acc + lv.col[v] + e, acc[v][e]);
+                } else if (p.direct_dw) {
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) p.dw[lv.col[v] + e] = (float)acc[v][e];
                 } else {
                     double2* dst = reinterpret_cast<double2*>(p.part + (int64_t)chunk * H + lv.col[v]);
 #pragma unroll
@@ -193,10 +223,10 @@ __global__ void __launch_bounds__(block_of(LPR)) bwd_kernel(BwdParams p)
             }
     }
 
-    if (p.atomic_form) {
+    if (p.form == FORM_ATOMIC) {
         // Every workgroup publishes its atomics (agent-scope fence) before it
         // takes a ticket; the one that draws the last ticket reads and clears
-        // the accumulator and writes dw.
+        // the accumulator and writes dw.  No workgroup ever waits for another.
         __threadfence();
         __syncthreads();
         if (tid == 0) {
@@ -217,36 +247,14 @@ __global__ void __launch_bounds__(block_of(LPR)) bwd_kernel(BwdParams p)
     }
 }
 
-// ------------------------------------------------ fixed-order dw reduce ----
-// dw[col] = sum over chunks of part[chunk][col].  A workgroup takes 16
-// columns; its 16 lane groups q sum chunks q, q+16, q+32, ... in that order
-// (16 loads in flight per lane), and the 16 group sums are added in q order.
-// The order depends only on the chunk count.
-constexpr int kReduceCols = 16;
-constexpr int kReduceGroups = 16;
-
 __global__ void __launch_bounds__(kReduceCols * kReduceGroups)
 dw_reduce_kernel(const double* __restrict__ part, int chunks, int H, float* __restrict__ dw)
 {
-    constexpr int DEPTH = 16;
     __shared__ double sums[kReduceGroups][kReduceCols];
     const int c = threadIdx.x % kReduceCols;
     const int q = threadIdx.x / kReduceCols;
     const int col = blockIdx.x * kReduceCols + c;
-    double s = 0.0;
-    if (col < H) {
-        for (int k = q; k < chunks; k += DEPTH * kReduceGroups) {
-            double a[DEPTH];
-#pragma unroll
-            for (int i = 0; i < DEPTH; ++i) {
-                const int kk = k + i * kReduceGroups;
-                a[i] = kk < chunks ? part[(int64_t)kk * H + col] : 0.0;
-            }
-#pragma unroll
-            for (int i = 0; i < DEPTH; ++i) s += a[i];
-        }
-    }
-    sums[q][c] = s;
+    sums[q][c] = col < H ? chunk_group_sum(part, chunks, H, col, q) : 0.0;
     __syncthreads();
     if (q == 0 && col < H) {
         double t = sums[0][c];

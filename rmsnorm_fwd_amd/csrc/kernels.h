@@ -34,7 +34,8 @@ struct BwdParams {
     int64_t stride_t, stride_h;
     int R, heads, H;
     int chunks;           // workgroups; workgroup c takes row groups c, c + chunks, ...
-    int atomic_form;
+    int form;             // FORM_PAIR or FORM_ATOMIC (route.h)
+    int direct_dw;        // pair form with one chunk: write dw, skip the reduce
     double inv_h;
 };
 

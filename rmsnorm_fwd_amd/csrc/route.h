@@ -9,6 +9,8 @@
 
 namespace rmsn {
 
+// pair: FP64 partials + fixed-order reduce kernel (with one chunk the row
+// kernel writes dw itself); atomic: FP64 atomic adds, last workgroup writes dw.
 enum { FORM_PAIR = 0, FORM_ATOMIC = 1 };
 
 struct BwdRoute {

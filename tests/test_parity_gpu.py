@@ -4,6 +4,8 @@ per-head views, both weight dtypes, residual in and out, both modes."""
 import numpy as np
 import pytest
 
+import oracle
+
 from tests.helpers import Layout, run_case
 
 pytestmark = pytest.mark.gpu
@@ -83,7 +85,7 @@ def test_routes_agree(H):
     # both sides of every route choice: pair and atomic forms at several
     # chunk counts (including more chunks than row groups); dx must be
     # bitwise the same for all of them and dw within budget for each
-    routes = [(0, 1), (0, 7), (0, 512), (0, 1000), (1, 1), (1, 5), (1, 256)]
+    routes = [(0, 1), (0, 2), (0, 7), (0, 512), (0, 1000), (1, 1), (1, 5), (1, 256)]
     rep = run_case(Layout.plain(333, H), "bf16", seed=21, routes=routes)
     print(H, rep)
 
@@ -92,3 +94,26 @@ def test_deterministic_dw_repeats_at_scale():
     # ten repeats of the deterministic backward on a large case
     rep = run_case(Layout.plain(16384, 4096), "f32", seed=2, det_repeats=10)
     print(rep)
+
+
+@pytest.mark.parametrize("H", [64, 256, 1536, 4096, 6144])
+@pytest.mark.parametrize("T", [1, 5, 300])
+def test_one_chunk_writes_dw_directly(T, H):
+    # with one chunk the row kernel writes dw itself; it must equal the
+    # reduce kernel's result for one partial bit for bit, and dx must not move
+    import torch
+    import rmsnorm_fwd_amd as rn
+    from tests.helpers import to_dev_bf16, weight_dev, gen_case, EPS
+    L = Layout.plain(T, H)
+    x, _, dy, _, w = gen_case(T + H, L, "bf16", False, False)
+    xd, dyd, wd = to_dev_bf16(x), to_dev_bf16(dy), weight_dev(w)
+    _, rstd, _ = rn.rmsnorm_fwd(xd, wd, EPS)
+    dx1, dw1 = rn.rmsnorm_bwd_routed(dyd, xd, rstd, wd, (rn.RMSN_FORM_PAIR, 1))
+    dx2, dw2 = rn.rmsnorm_bwd_routed(dyd, xd, rstd, wd, (rn.RMSN_FORM_PAIR, 1))
+    dx3, dw3 = rn.rmsnorm_bwd_routed(dyd, xd, rstd, wd, (rn.RMSN_FORM_PAIR, 2))
+    torch.cuda.synchronize()
+    assert torch.equal(dw1, dw2) and torch.equal(dx1, dx3)
+    ref = oracle.dw_bf16(x, dy, rstd.cpu().numpy())
+    from tests.helpers import check_dw, Report
+    check_dw(dw1.cpu().numpy(), ref, Report())
+    check_dw(dw3.cpu().numpy(), ref, Report())
