@@ -208,8 +208,8 @@ def profiled_traffic(workload, kernel):
     rec = json.loads(m.group(1)).get("kernels", {}).get(kernel)
     if not rec:
         return None
-    srcs = {"fwd_kernel": ["fwd.hip", "device_common.h", "layouts.h"],
-            "bwd_kernel": ["bwd.hip", "device_common.h", "layouts.h"]}[kernel]
+    srcs = {"fwd_kernel": ["fwd.hip", "device_common.h", "kernels.h", "layouts.h"],
+            "bwd_kernel": ["bwd.hip", "device_common.h", "kernels.h", "layouts.h"]}[kernel]
     h = hashlib.sha256()
     for f in srcs:
         with open(os.path.join(ROOT, "rmsnorm_fwd_amd", "csrc", f), "rb") as fh:

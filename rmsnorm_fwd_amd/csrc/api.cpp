@@ -88,10 +88,8 @@ int bwd_impl(const void* dy, const void* x, const float* rstd, const void* w, in
     p.ticket = reinterpret_cast<unsigned*>(ws);
     p.acc = reinterpret_cast<double*>(ws + ws_acc_offset());
     p.part = reinterpret_cast<double*>(ws + ws_part_offset(s.H));
-    p.stride_t = s.st;
-    p.stride_h = s.sh;
+    p.rows = make_row_map(s.heads, s.st, s.sh);
     p.R = (int)s.R;
-    p.heads = (int)s.heads;
     p.H = (int)s.H;
     p.chunks = r.chunks;
     p.form = r.form;
@@ -154,10 +152,8 @@ int rmsnorm_fwd(const void* x, const void* residual, const void* w, int w_dtype,
     p.y = static_cast<uint16_t*>(y);
     p.h = static_cast<uint16_t*>(residual_out);
     p.rstd = rstd;
-    p.stride_t = s.st;
-    p.stride_h = s.sh;
+    p.rows = make_row_map(s.heads, s.st, s.sh);
     p.R = (int)s.R;
-    p.heads = (int)s.heads;
     p.H = (int)s.H;
     p.eps = eps;
     p.inv_h = 1.0 / (double)s.H;

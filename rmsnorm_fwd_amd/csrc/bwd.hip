@@ -19,7 +19,8 @@
 // lane does not own).
 //
 // dw.  Each lane keeps FP64 column sums over the chunk's rows in registers;
-// row groups of one workgroup are added in LDS in slot order.  With a single
+// row groups of one workgroup are added by lane exchanges inside a
+// wavefront, then across wavefronts through LDS, in a fixed order.  With a single
 // chunk that sum is dw and is written directly; otherwise the chunk sum goes
 //   pair form:   to row `chunk` of a workspace [chunks, H] (FP64), summed by
 //                dw_reduce_kernel in a fixed order -- deterministic;
@@ -76,7 +77,7 @@ __device__ __forceinline__ void bwd_load(BwdTile<U, V>& t, const BwdParams& p, c
         const int row = base + u * SLOTS + slot;
         t.ok[u] = row < row1;
         const int rr = t.ok[u] ? row : row1 - 1;  // rows past the end re-read the last row
-        t.off[u] = row_offset(rr, p.heads, p.stride_t, p.stride_h);
+        t.off[u] = row_offset(rr, p.rows);
         t.rho[u] = t.ok[u] ? (double)p.rstd[rr] : 0.0;  // ... and add nothing to dw
     }
 #pragma unroll
@@ -97,7 +98,7 @@ __global__ void __launch_bounds__(block_of(LPR)) bwd_kernel(BwdParams p)
     constexpr int RPI = SLOTS * U;
     __shared__ double red[2][RPI][W];
     __shared__ int last_block;
-    extern __shared__ double slot_part[];  // [SLOTS][H] when SLOTS > 1
+    extern __shared__ double slot_part[];  // [wavefronts][H] when SLOTS > 1
 
     const int tid = threadIdx.x;
     const int g = tid % LPR;
@@ -190,17 +191,36 @@ __global__ void __launch_bounds__(block_of(LPR)) bwd_kernel(BwdParams p)
 
     // ---- chunk sum of dw ----------------------------------------------
     if constexpr (SLOTS > 1) {
+        // Row groups of this workgroup hold column sums for the same
+        // columns.  Those sharing a wavefront are added with a butterfly of
+        // lane exchanges (every lane ends with the wavefront's sum); each
+        // wavefront's first row group then stores that sum in its own LDS
+        // row, and the rows are added in wavefront order.  Fixed order
+        // throughout; LDS use is (BLOCK/max(LPR,64)) * H doubles.
+        constexpr int SPW = LPR < 64 ? 64 / LPR : 1;  // row groups per wavefront
+        constexpr int GROUPS = SLOTS / SPW;
+        if constexpr (SPW > 1) {
 #pragma unroll
-        for (int v = 0; v < V; ++v)
-            if (lv.ok[v]) {
+            for (int off = LPR; off < 64; off <<= 1)
 #pragma unroll
-                for (int e = 0; e < 8; ++e) slot_part[slot * H + lv.col[v] + e] = acc[v][e];
-            }
+                for (int v = 0; v < V; ++v)
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) acc[v][e] += __shfl_xor(acc[v][e], off);
+        }
+        if (slot % SPW == 0) {
+            double* row = slot_part + (slot / SPW) * H;
+#pragma unroll
+            for (int v = 0; v < V; ++v)
+                if (lv.ok[v]) {
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) row[lv.col[v] + e] = acc[v][e];
+                }
+        }
         __syncthreads();
         for (int col = tid; col < H; col += BLOCK) {
             double s = slot_part[col];
 #pragma unroll
-            for (int sl = 1; sl < SLOTS; ++sl) s += slot_part[sl * H + col];
+            for (int gi = 1; gi < GROUPS; ++gi) s += slot_part[gi * H + col];
             if (p.form == FORM_ATOMIC) unsafeAtomicAdd(p.acc + col, s);
             else if (p.direct_dw) p.dw[col] = (float)s;
             else p.part[(int64_t)chunk * H + col] = s;
@@ -277,7 +297,8 @@ template <int LPR, int V, int U, bool WF32, bool DRES>
 static hipError_t bwd_t(const BwdParams& p, hipStream_t s)
 {
     constexpr int SLOTS = slots_of(LPR);
-    const size_t lds = SLOTS > 1 ? (size_t)SLOTS * p.H * sizeof(double) : 0;
+    constexpr int ROWS = LPR < 64 ? block_of(LPR) / 64 : SLOTS;
+    const size_t lds = SLOTS > 1 ? (size_t)ROWS * p.H * sizeof(double) : 0;
     if (lds > (size_t)kMaxSlotLds) return hipErrorInvalidConfiguration;
     hipLaunchKernelGGL((bwd_kernel<LPR, V, U, WF32, DRES>), dim3(p.chunks), dim3(block_of(LPR)), lds, s, p);
     return hipGetLastError();

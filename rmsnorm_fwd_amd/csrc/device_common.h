@@ -6,6 +6,7 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "kernels.h"
 #include "layouts.h"
 
 namespace rmsn {
@@ -124,12 +125,14 @@ __device__ __forceinline__ double group_sum_f64(double v)
     return v;
 }
 
-__device__ __forceinline__ int64_t row_offset(int row, int heads, int64_t st, int64_t sh)
+__device__ __forceinline__ int64_t row_offset(int row, const RowMap& m)
 {
-    if (heads == 1) return (int64_t)row * st;
-    const int t = row / heads;
-    const int hd = row - t * heads;
-    return (int64_t)t * st + (int64_t)hd * sh;
+    if (m.heads == 1) return (int64_t)row * m.stride_t;
+    const uint32_t n = (uint32_t)row;
+    const uint32_t hi = __umulhi(n, m.magic);
+    const uint32_t t = (hi + ((n - hi) >> 1)) >> (m.shift - 1);
+    const uint32_t hd = n - t * m.heads;
+    return (int64_t)t * m.stride_t + (int64_t)hd * m.stride_h;
 }
 
 // 1/sqrt(m) in FP64: hardware estimate refined by two Newton steps, then

@@ -36,7 +36,7 @@ __device__ __forceinline__ void fwd_load(FwdTile<U, V, RES>& t, const FwdParams&
     for (int u = 0; u < U; ++u) {
         t.row[u] = base + u * SLOTS + slot;
         t.ok[u] = t.row[u] < p.R;
-        t.off[u] = row_offset(t.ok[u] ? t.row[u] : p.R - 1, p.heads, p.stride_t, p.stride_h);
+        t.off[u] = row_offset(t.ok[u] ? t.row[u] : p.R - 1, p.rows);
     }
 #pragma unroll
     for (int u = 0; u < U; ++u)

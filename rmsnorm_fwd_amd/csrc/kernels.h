@@ -8,6 +8,30 @@
 
 namespace rmsn {
 
+// Where row r = t * heads + head of a [T, heads, H] tensor starts:
+// t * stride_t + head * stride_h elements.  t = r / heads is taken by the
+// multiply-shift method for invariant divisors (Granlund and Montgomery,
+// "Division by invariant integers using multiplication", 1994), valid for
+// every 32-bit r: with l = ceil(log2(heads)) and
+// magic = floor(2^32 (2^l - heads) / heads) + 1,
+// t = (hi + ((r - hi) >> 1)) >> (l - 1), hi = the high 32 bits of r * magic.
+struct RowMap {
+    int64_t stride_t, stride_h;
+    uint32_t heads, magic, shift;
+};
+
+inline RowMap make_row_map(int64_t heads, int64_t stride_t, int64_t stride_h)
+{
+    RowMap m{stride_t, stride_h, (uint32_t)heads, 0u, 0u};
+    if (heads > 1) {
+        uint32_t l = 0;
+        while ((1ull << l) < (uint64_t)heads) ++l;
+        m.magic = (uint32_t)(((1ull << 32) * ((1ull << l) - (uint64_t)heads)) / (uint64_t)heads + 1);
+        m.shift = l;
+    }
+    return m;
+}
+
 struct FwdParams {
     const uint16_t* x;    // [T,heads,H] BF16
     const uint16_t* r;    // residual or nullptr
@@ -15,8 +39,8 @@ struct FwdParams {
     uint16_t* y;          // [T,heads,H] BF16
     uint16_t* h;          // residual output (when r != nullptr)
     float* rstd;          // [R]
-    int64_t stride_t, stride_h;
-    int R, heads, H;
+    RowMap rows;
+    int R, H;
     double eps, inv_h;
 };
 
@@ -31,8 +55,8 @@ struct BwdParams {
     double* part;         // [P,H] FP64 chunk partials (pair form)
     double* acc;          // [H] FP64 accumulator (atomic form), zero on entry and exit
     unsigned* ticket;     // arrival counter (atomic form), zero on entry and exit
-    int64_t stride_t, stride_h;
-    int R, heads, H;
+    RowMap rows;
+    int R, H;
     int chunks;           // workgroups; workgroup c takes row groups c, c + chunks, ...
     int form;             // FORM_PAIR or FORM_ATOMIC (route.h)
     int direct_dw;        // pair form with one chunk: write dw, skip the reduce

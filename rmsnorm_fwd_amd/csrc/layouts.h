@@ -35,7 +35,7 @@ struct Layout {
 #define RMSN_FWD_LAYOUTS(X)    \
     X(0, 64, 8, 1, 4, 64)      \
     X(1, 128, 16, 1, 4, 64)    \
-    X(2, 256, 16, 2, 2, 64)    \
+    X(2, 256, 8, 4, 1, 64)     \
     X(3, 512, 32, 2, 2, 64)    \
     X(4, 1024, 32, 4, 1, 64)   \
     X(5, 1536, 32, 6, 1, 16)   \
@@ -67,11 +67,13 @@ RMSN_FWD_LAYOUTS(RMSN_CHECK_LAYOUT)
 RMSN_BWD_LAYOUTS(RMSN_CHECK_LAYOUT)
 #undef RMSN_CHECK_LAYOUT
 
-// The backward combines its row groups' FP64 column sums in LDS:
-// SLOTS * H * 8 bytes, which must stay within kMaxSlotLds.
+// The backward adds its row groups' FP64 column sums through LDS, one row
+// of H doubles per wavefront (per row group when a row group spans
+// wavefronts): at most (256 / min(LPR, 64)) * H * 8 bytes when LPR < 256,
+// which must stay within kMaxSlotLds.
 constexpr long kMaxSlotLds = 64 * 1024;
-#define RMSN_CHECK_LDS(id, mh, l, vv, uu, kk)                                                   \
-    static_assert((l) >= 256 || (256 / (l)) == 1 || (long)(256 / (l)) * (mh) * 8 <= kMaxSlotLds, \
+#define RMSN_CHECK_LDS(id, mh, l, vv, uu, kk)                                                        \
+    static_assert((l) >= 256 || (long)(256 / ((l) < 64 ? 64 : (l))) * (mh) * 8 <= kMaxSlotLds, \
                   "backward layout needs too much LDS");
 RMSN_BWD_LAYOUTS(RMSN_CHECK_LDS)
 #undef RMSN_CHECK_LDS
