@@ -1,5 +1,5 @@
 // kernels.h -- internal interface between the C-ABI layer (api.cpp) and the
-// HIP kernels (kernels.hip).  Not installed; the public ABI is
+// HIP kernels (fwd.hip, bwd.hip).  Not installed; the public ABI is
 // include/rmsnorm.h.
 #pragma once
 

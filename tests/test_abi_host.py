@@ -146,3 +146,15 @@ def test_status_strings():
     for s in range(6):
         assert rn.status_string(s)
     assert rn.status_string(99) == "unknown status"
+
+
+def test_row_map_division_is_exact(tmp_path):
+    # compiled with the host compiler against the library's internal header
+    src = os.path.join(ROOT, "tests", "host", "row_map_check.cpp")
+    exe = str(tmp_path / "row_map_check")
+    csrc = os.path.join(ROOT, "rmsnorm_fwd_amd", "csrc")
+    subprocess.run(["g++", "-O2", "-std=c++17", "-D__HIP_PLATFORM_AMD__", f"-I{csrc}", "-I/opt/rocm/include",
+                    src, "-o", exe], check=True)
+    out = subprocess.run([exe], capture_output=True, text=True)
+    assert out.returncode == 0, out.stdout
+    assert " 0 failures" in out.stdout
