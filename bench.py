@@ -130,22 +130,37 @@ class Workload:
         self.bwd(det)
 
 
-def time_cold(fn, reps, flush_buf):
-    """Median/p10/p90 microseconds of fn with L2 and last-level cache flushed
-    before each launch (a 1 GiB write on the same stream, outside the events)."""
+def time_cold(ops, rounds, reps, flush_buf):
+    """Cache-flushed launch times (us) of every op in `ops` (name -> fn).
+
+    Before each launch L2 and the last-level cache are flushed by a 1 GiB
+    write on the same stream, outside the events.  The ops are interleaved
+    launch by launch, in an order rotated every round, so that drift of the
+    machine hits all of them alike.  Returns name -> list of `rounds` lists."""
     import torch
 
-    ts = []
-    for _ in range(reps):
-        flush_buf.fill_(1)
-        a = torch.cuda.Event(enable_timing=True)
-        b = torch.cuda.Event(enable_timing=True)
-        a.record()
-        fn()
-        b.record()
-        b.synchronize()
-        ts.append(a.elapsed_time(b) * 1e3)
-    return {"median_us": statistics.median(ts), "p10_us": percentile(ts, 10), "p90_us": percentile(ts, 90)}
+    names = list(ops)
+    out = {n: [[] for _ in range(rounds)] for n in names}
+    a = torch.cuda.Event(enable_timing=True)
+    b = torch.cuda.Event(enable_timing=True)
+    for rd in range(rounds):
+        order = names[rd % len(names):] + names[:rd % len(names)]
+        for _ in range(reps):
+            for n in order:
+                flush_buf.fill_(1)
+                a.record()
+                ops[n]()
+                b.record()
+                b.synchronize()
+                out[n][rd].append(a.elapsed_time(b) * 1e3)
+    return out
+
+
+def summarize(rounds_us):
+    ts = [t for r in rounds_us for t in r]
+    return {"median_us": round(statistics.median(ts), 2), "p10_us": round(percentile(ts, 10), 2),
+            "p90_us": round(percentile(ts, 90), 2), "launches": len(ts),
+            "round_medians_us": [round(statistics.median(r), 2) for r in rounds_us]}
 
 
 def time_warm(fn, reps):
@@ -163,11 +178,22 @@ def time_warm(fn, reps):
     return a.elapsed_time(b) * 1e3 / reps
 
 
+def cpu_model():
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
+
+
 def cpu_baseline(wl: Workload, min_seconds=10.0, max_seconds=30.0):
     """The oracle (FP64, OpenMP) on the host: fwd + fwd + bwd over a bounded
     sample of the workload's rows, as GB/s of the same byte model.  The
     sample is the whole workload when one step takes under ~10 s, else the
-    leading rows; the step repeats until about 10 s of work is done."""
+    leading rows; the step repeats until about 10 s of work is done.  The
+    forward and backward are also timed on their own (medians)."""
     import oracle
 
     nthreads = oracle.num_threads()
@@ -176,20 +202,22 @@ def cpu_baseline(wl: Workload, min_seconds=10.0, max_seconds=30.0):
     _step_oracle(wl, probe_rows)
     per_row = (time.time() - t0) / probe_rows
     rows = int(min(wl.R, max(probe_rows, 10.0 / max(per_row, 1e-9))))
-    reps = []
+    steps, fwds, bwds = [], [], []
     t_start = time.time()
-    while (time.time() - t_start) < min_seconds or len(reps) < 3:
-        t0 = time.time()
-        _step_oracle(wl, rows)
-        reps.append(time.time() - t0)
+    while (time.time() - t_start) < min_seconds or len(steps) < 3:
+        tf1, tf2, tb = _step_oracle(wl, rows)
+        steps.append(tf1 + tf2 + tb)
+        fwds += [tf1, tf2]
+        bwds.append(tb)
         if time.time() - t_start > max_seconds:
             break
-    sec = statistics.median(reps)
+    sec = statistics.median(steps)
     sample_bytes = 2 * fwd_bytes(rows, wl.H, wl.sw, wl.res) + bwd_bytes(rows, wl.H, wl.sw, False)
     return {"value": sample_bytes / sec / 1e9, "unit": "GB/s", "cores": nthreads, "kind": "oracle",
-            "sample": f"2xfwd+bwd over rows 0..{rows - 1} of {wl.R} (H={wl.H}), median of {len(reps)} "
+            "sample": f"2xfwd+bwd over rows 0..{rows - 1} of {wl.R} (H={wl.H}), median of {len(steps)} "
                       f"repeats, {sec:.2f} s per step, {time.time() - t_start:.1f} s in all",
-            "step_seconds": sec, "rows": rows}
+            "step_seconds": sec, "fwd_seconds": statistics.median(fwds), "bwd_seconds": statistics.median(bwds),
+            "rows": rows, "cpu_model": cpu_model()}
 
 
 def profiled_traffic(workload, kernel):
@@ -217,18 +245,110 @@ def profiled_traffic(workload, kernel):
     return rec["traffic_bytes"] if h.hexdigest()[:16] == rec["source_hash"] else None
 
 
+# The pages' latency tables (p1 #8577, per-shape fwd/bwd/step rows) cover
+# T = 1..64 at H = 2048, 4096 (BF16 and FP32 w), 5120 and 6144 (plain, FP32
+# w, residual, residual with FP32 w).  (H, T, w dtype, residual):
+SMALL_T_SHAPES = (
+    [(H, T, w, False) for H in (2048, 4096) for T in (1, 4, 16, 64) for w in ("bf16", "f32")]
+    + [(5120, T, "bf16", False) for T in (1, 4, 16, 64)]
+    + [(6144, T, w, r) for T in (1, 4, 16, 64) for w in ("bf16", "f32") for r in (False, True)])
+
+# The whole shape list of those tables (bench.py --shape-sweep).
+SWEEP_SHAPES = (
+    [(H, T, "bf16", False) for H in (512, 1536) for T in (256, 1024, 4096, 14928, 16384, 32768, 65536)]
+    + [(H, T, w, False) for H in (2048, 4096) for T in (1, 4, 16, 64) for w in ("bf16", "f32")]
+    + [(H, T, "bf16", False) for H in (2048, 4096) for T in (256, 1024, 4096, 14928, 16384, 32768, 65536)]
+    + [(5120, T, "bf16", False) for T in (1, 4, 16, 64, 321, 512, 896)]
+    + [(5120, T, w, False) for T in (256, 1024, 4096, 14928, 16384, 32768, 65536) for w in ("bf16", "f32")]
+    + [(6144, T, w, r) for T in (1, 4, 16, 64, 256, 1024, 4096, 14928, 16384, 32768, 65536)
+       for w in ("bf16", "f32") for r in (False, True)]
+    + [(6144, T, w, False) for T in (449, 768, 1152) for w in ("bf16", "f32")])
+
+
+def shape_name(H, T, wdt, res):
+    return f"H{H} T{T}" + (" res" if res else "") + (" w32" if wdt == "f32" else "")
+
+
+class DeviceCase:
+    """Inputs of one (H, T, w dtype, residual) shape drawn on the device from
+    a seeded torch generator (latency does not depend on the values), x, r,
+    dy ~ N(0,1), w = 1 + 0.1 N(0,1)."""
+
+    def __init__(self, H, T, wdt, res, seed=0):
+        import torch
+
+        import rmsnorm_fwd_amd as rn
+
+        g = torch.Generator(device="cuda")
+        g.manual_seed(seed)
+        bf = torch.bfloat16
+        self.rn, self.res = rn, res
+        self.x = torch.randn(T, H, generator=g, device="cuda").to(bf)
+        self.r = torch.randn(T, H, generator=g, device="cuda").to(bf) if res else None
+        self.dy = torch.randn(T, H, generator=g, device="cuda").to(bf)
+        w = 1 + 0.1 * torch.randn(H, generator=g, device="cuda")
+        self.w = w if wdt == "f32" else w.to(bf)
+        self.y = torch.empty_like(self.x)
+        self.h = torch.empty_like(self.x) if res else None
+        self.dx = torch.empty_like(self.x)
+        self.rstd = torch.empty(T, dtype=torch.float32, device="cuda")
+        self.dw = torch.empty(H, dtype=torch.float32, device="cuda")
+        self.ws = rn.rmsnorm_bwd_workspace(T, 1, H, "cuda")
+
+    def fwd(self):
+        self.rn.rmsnorm_fwd(self.x, self.w, EPS, residual=self.r, y=self.y, residual_out=self.h,
+                            rstd=self.rstd)
+
+    def bwd(self, det=True):
+        self.rn.rmsnorm_bwd(self.dy, self.h if self.res else self.x, self.rstd, self.w, deterministic=det,
+                            dx=self.dx, dw=self.dw, workspace=self.ws)
+
+    def step(self):
+        self.fwd()
+        self.fwd()
+        self.bwd(True)
+
+
+def shape_latencies(shapes, flush_buf, rounds, reps):
+    """Cache-flushed median latency (us) of fwd, bwd (both modes) and the
+    deterministic 2xfwd+bwd step for each shape, plus the floor: the same
+    timing around a one-element torch fill."""
+    import torch
+
+    tiny = torch.empty(1, dtype=torch.float32, device="cuda")
+    floor = time_cold({"fill": lambda: tiny.fill_(0)}, rounds, reps, flush_buf)["fill"]
+    rows = []
+    for H, T, wdt, res in shapes:
+        c = DeviceCase(H, T, wdt, res)
+        ops = {"fwd": c.fwd, "bwd_det": lambda: c.bwd(True), "bwd_nondet": lambda: c.bwd(False),
+               "step_det": c.step}
+        for fn in ops.values():
+            fn()
+        raw = time_cold(ops, rounds, reps, flush_buf)
+        row = {"shape": shape_name(H, T, wdt, res)}
+        for k, v in raw.items():
+            row[k + "_us"] = round(statistics.median([t for r in v for t in r]), 2)
+        rows.append(row)
+        del c
+    return {"floor_us": round(statistics.median([t for r in floor for t in r]), 2),
+            "launches_per_op": rounds * reps, "rows": rows}
+
+
 def _step_oracle(wl, rows):
+    """One oracle step over the leading `rows` rows; seconds of its three ops."""
     import oracle
 
-    H = wl.H
     x = _rows_view(wl.x_h, rows)
     r = _rows_view(wl.r_h, rows) if wl.res else None
     dy = _rows_view(wl.dy_h, rows)
+    t0 = time.perf_counter()
     oracle.fwd_bf16(x, wl.w_h, EPS, r)
+    t1 = time.perf_counter()
     y, h, rstd = oracle.fwd_bf16(x, wl.w_h, EPS, r)
-    u = h if wl.res else x
-    oracle.bwd_bf16(u, dy, wl.w_h, rstd.astype(np.float32))
-    return H
+    t2 = time.perf_counter()
+    oracle.bwd_bf16(h if wl.res else x, dy, wl.w_h, rstd.astype(np.float32))
+    t3 = time.perf_counter()
+    return t1 - t0, t2 - t1, t3 - t2
 
 
 def _rows_view(a, rows):
@@ -241,7 +361,12 @@ def main():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default=DEFAULT_WORKLOAD, choices=sorted(WORKLOADS))
-    ap.add_argument("--cold-reps", type=int, default=60, help="launches per op for the cache-flushed latency")
+    ap.add_argument("--cold-reps", type=int, default=210,
+                    help="cache-flushed launches per op, split over --cold-rounds interleaved rounds")
+    ap.add_argument("--cold-rounds", type=int, default=3)
+    ap.add_argument("--no-small-t", action="store_true", help="skip the small-T latency sweep")
+    ap.add_argument("--shape-sweep", action="store_true",
+                    help="also time every shape of the pages' latency tables (a few minutes)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--profile", action="store_true",
                     help="only warmup + timed steps (for rocprofv3 runs), no per-op extras")
@@ -312,28 +437,42 @@ def main():
     }
 
     if not args.profile:
-        # per-op latency, cold caches
+        # per-op latency, cold caches; "fwd_aa" is the forward again, timed as
+        # if it were another implementation (the A/A floor of the method)
         flush = torch.empty(1 << 28, dtype=torch.float32, device="cuda")  # 1 GiB
         ops = {
             "fwd": (wl.fwd, wl.fwd_bytes),
+            "fwd_aa": (wl.fwd, wl.fwd_bytes),
             "bwd_det": (lambda: wl.bwd(True), wl.bwd_bytes),
             "bwd_nondet": (lambda: wl.bwd(False), wl.bwd_bytes),
             "step_det": (lambda: wl.step(True), wl.step_bytes),
             "step_nondet": (lambda: wl.step(False), wl.step_bytes),
         }
-        lat = {}
-        for name, (fn, nbytes) in ops.items():
+        for fn, _ in ops.values():
             for _ in range(3):
                 fn()
-            c = time_cold(fn, args.cold_reps, flush)
+        reps = max(1, -(-args.cold_reps // args.cold_rounds))
+        raw = time_cold({k: v[0] for k, v in ops.items()}, args.cold_rounds, reps, flush)
+        lat = {}
+        for name, (_, nbytes) in ops.items():
+            c = summarize(raw[name])
             c["gbs"] = round(nbytes / (c["median_us"] * 1e-6) / 1e9, 1)
             c["pct_peak"] = round(100 * c["gbs"] / PEAK_GBS, 2)
             c["bytes"] = nbytes
-            for k in ("median_us", "p10_us", "p90_us"):
-                c[k] = round(c[k], 2)
             lat[name] = c
             log(f"cold {name}: {c['median_us']:.1f} us  {c['gbs']:.0f} GB/s ({c['pct_peak']:.1f}%)")
+        lat["aa_floor_pct"] = round(100 * abs(lat["fwd"]["median_us"] - lat["fwd_aa"]["median_us"])
+                                    / lat["fwd"]["median_us"], 3)
         out["latency_cold"] = lat
+
+        if not args.no_small_t:
+            t0 = time.time()
+            out["small_t"] = shape_latencies(SMALL_T_SHAPES, flush, args.cold_rounds, 20)
+            log(f"small-T latencies: {len(SMALL_T_SHAPES)} shapes in {time.time() - t0:.1f}s")
+        if args.shape_sweep:
+            t0 = time.time()
+            out["shape_sweep"] = shape_latencies(SWEEP_SHAPES, flush, args.cold_rounds, 20)
+            log(f"shape sweep: {len(SWEEP_SHAPES)} shapes in {time.time() - t0:.1f}s")
 
         # roofline of the dominant kernels: per-launch duration from HIP events
         # around back-to-back launches on the stream the library uses

@@ -158,3 +158,17 @@ def test_row_map_division_is_exact(tmp_path):
     out = subprocess.run([exe], capture_output=True, text=True)
     assert out.returncode == 0, out.stdout
     assert " 0 failures" in out.stdout
+
+
+def test_route_chunk_count_grows_with_rows_and_stays_bounded():
+    # one workgroup per chunk: never more than 512 (two per compute unit), one
+    # for the smallest inputs, and never fewer as the row count grows
+    for H in (256, 1536, 4096, 5120, 6144, 16384):
+        prev = 0
+        for T in [1, 2, 3, 4, 7, 16, 64, 100, 256, 449, 512, 1024, 2048, 4096, 16384, 65536, 131072]:
+            form, chunks = rn.rmsnorm_bwd_route(T, 1, H, 0, 0, 1)
+            assert form == rn.RMSN_FORM_PAIR
+            assert 1 <= chunks <= min(512, T) and chunks >= prev, (H, T, chunks)
+            prev = chunks
+        assert rn.rmsnorm_bwd_route(1, 1, H, 0, 0, 1)[1] == 1
+        assert prev >= 256
