@@ -54,9 +54,9 @@ struct Layout {
     X(3, 512, 32, 2, 2, 512)      \
     X(4, 1024, 64, 2, 1, 512)     \
     X(5, 1536, 64, 3, 1, 512)     \
-    X(6, 2048, 128, 2, 1, 512)    \
+    X(6, 2048, 128, 2, 2, 512)    \
     X(7, 3072, 128, 3, 1, 512)    \
-    X(8, 4096, 256, 2, 1, 512)    \
+    X(8, 4096, 256, 2, 2, 512)    \
     X(9, 6144, 256, 3, 1, 512)    \
     X(10, 8192, 1024, 1, 1, 256)  \
     X(11, 16384, 512, 4, 1, 256)
