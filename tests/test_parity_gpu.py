@@ -117,3 +117,90 @@ def test_one_chunk_writes_dw_directly(T, H):
     from tests.helpers import check_dw, Report
     check_dw(dw1.cpu().numpy(), ref, Report())
     check_dw(dw3.cpu().numpy(), ref, Report())
+
+
+@pytest.mark.parametrize("heads", [1, 3])
+def test_offsets_beyond_32_bits(heads):
+    # rows (or tokens) 2^30 + 1536 elements apart: the last rows start past
+    # 2^32 elements (8 GiB) into their buffers, so every row address needs
+    # 64-bit arithmetic.  Rows are compared with the oracle; the elements on
+    # both sides of every row must keep their sentinel.
+    import torch
+    import rmsnorm_fwd_amd as rn
+    from tests.helpers import (EPS, SENTINEL, Report, check_dw, check_dx, check_fwd, gen_case,
+                               to_host_bits, weight_dev)
+    T, H = 5, 1536
+    L = Layout.heads_view(T, heads, H, (1 << 30) + 1536, H if heads == 1 else 2048)
+    assert (T - 1) * L.stride_t > (1 << 32)
+    x, _, dy, _, w = gen_case(31, L, "bf16", False, False)
+    xb, dyb, yb, dxb = L.place(x), L.place(dy), L.empty(), L.empty()
+    wd = weight_dev(w)
+    rstd = torch.empty(L.R, dtype=torch.float32, device="cuda")
+    rn.rmsnorm_fwd(L.view(xb), wd, EPS, y=L.view(yb), rstd=rstd)
+    dw = torch.empty(H, dtype=torch.float32, device="cuda")
+    rn.rmsnorm_bwd(L.view(dyb), L.view(xb), rstd, wd, dx=L.view(dxb), dw=dw)
+    torch.cuda.synchronize()
+    rep = Report()
+    ref_y, _, ref_rstd = oracle.fwd_bf16(x, w, EPS)
+    rstd_h = rstd.cpu().numpy()
+    check_fwd(L.rows_of(yb), None, rstd_h, ref_y, None, ref_rstd, rep)
+    ref_dx, _, ref_dw = oracle.bwd_bf16(x, dy, w, rstd_h)
+    check_dx(L.rows_of(dxb), ref_dx, rep)
+    check_dw(dw.cpu().numpy(), ref_dw, rep)
+    for buf in (yb, dxb):
+        for t in range(T):
+            for hd in range(heads):
+                s = t * L.stride_t + hd * L.stride_h
+                for lo, hi in ((s - 8, s), (s + H, s + H + 8)):
+                    lo, hi = max(lo, 0), min(hi, L.buffer_elems())
+                    if lo < hi:
+                        assert np.all(to_host_bits(buf[lo:hi]) == SENTINEL), (t, hd, lo)
+    print(heads, rep)
+
+
+def test_max_rows_periodic():
+    # The largest row count the library takes, R = 2^30 - 1, at H = 8.  The
+    # rows repeat a block of P seeded rows, so the oracle needs only the
+    # block: sampled rows of y, rstd and dx must match the oracle's values
+    # for their block row, and dw = (R // P) * dw(block) + dw(first R % P
+    # rows of the block) in FP64.
+    import torch
+    import rmsnorm_fwd_amd as rn
+    from tests.helpers import (EPS, Report, check_dw, check_dx, check_fwd, gen_case, to_dev_bf16,
+                               to_host_bits, weight_dev)
+    H, P = 8, 4096
+    R = (1 << 30) - 1
+    reps, rem = divmod(R, P)
+    x, _, dy, _, w = gen_case(41, Layout.plain(P, H), "f32", False, False)
+    wd = weight_dev(w)
+
+    def tiled(rows):
+        blk = to_dev_bf16(rows).view(P, H)
+        t = torch.empty(R, H, dtype=torch.bfloat16, device="cuda")
+        t[:reps * P].view(reps, P, H).copy_(blk.unsqueeze(0).expand(reps, P, H))
+        t[reps * P:].copy_(blk[:rem])
+        return t
+
+    X, DY = tiled(x), tiled(dy)
+    y, rstd, _ = rn.rmsnorm_fwd(X, wd, EPS)
+    rng = np.random.default_rng(3)
+    sample = np.unique(np.concatenate([[0, 1, P - 1, P, R - rem - 1, R - rem, R - 1],
+                                       rng.integers(0, R, 2000)]))
+    idx = torch.from_numpy(sample).cuda()
+    base = sample % P
+    rstd_blk = rstd[:P].cpu().numpy()
+    rep = Report()
+    ref_y, _, ref_rstd = oracle.fwd_bf16(x, w, EPS)
+    check_fwd(to_host_bits(y[idx]), None, rstd[idx].cpu().numpy(), ref_y[base], None, ref_rstd[base], rep)
+    assert np.array_equal(rstd[idx].cpu().numpy(), rstd_blk[base]), "a repeated row got another rstd"
+    ref_dx, _, ref_dw_blk = oracle.bwd_bf16(x, dy, w, rstd_blk)
+    _, _, ref_dw_rem = oracle.bwd_bf16(x[:rem], dy[:rem], w, rstd_blk[:rem])
+    ref_dw = reps * ref_dw_blk + ref_dw_rem
+    del y
+    for det in (True, False):
+        dx, dw = rn.rmsnorm_bwd(DY, X, rstd, wd, deterministic=det)
+        torch.cuda.synchronize()
+        check_dx(to_host_bits(dx[idx]), ref_dx[base], rep)
+        check_dw(dw.cpu().numpy(), ref_dw, rep)
+        del dx
+    print(rep)
