@@ -39,9 +39,9 @@ struct Layout {
     X(3, 512, 32, 2, 2, 64)    \
     X(4, 1024, 32, 4, 1, 64)   \
     X(5, 1536, 32, 6, 1, 16)   \
-    X(6, 2048, 32, 8, 1, 32)   \
+    X(6, 2048, 256, 1, 4, 32)  \
     X(7, 3072, 64, 6, 1, 32)   \
-    X(8, 4096, 256, 2, 2, 16)  \
+    X(8, 4096, 512, 1, 2, 32)  \
     X(9, 5120, 128, 5, 1, 16)  \
     X(10, 6144, 768, 1, 2, 16) \
     X(11, 8192, 512, 2, 2, 32) \
