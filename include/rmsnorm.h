@@ -14,9 +14,9 @@
  *             dx = rstd * (w * dy - xhat * c) [+ dres]   (BF16)
  *             dw = sum over all rows of dy * xhat         (FP32)
  *             with deterministic = 1 (fixed-order, bitwise reproducible dw)
- *             or 0 (atomic dw, reproducible only within its error budget);
- *             dx is bitwise the same in both modes (p1 #8208 commit message:
- *             "dx is the same bit for bit across calls").
+ *             or 0 (dw reproducible only within its error budget);
+ *             dx is bitwise the same in both modes and from call to call
+ *             (p1 #8208 commit message).
  *
  * Tensors.  Every activation tensor (x, r, h, y, dy, dres, dx) is BF16 with
  * the logical shape [T, heads, H] and element strides (stride_t, stride_h, 1);
@@ -33,7 +33,7 @@
  *
  * Requirements checked on entry (violations return an error, nothing runs):
  *   - H % 8 == 0 and 8 <= H <= RMSN_MAX_H                  else RMSN_ERR_UNSUPPORTED
- *   - T >= 0, heads >= 1, R = T*heads < 2^31, eps finite >= 0
+ *   - T >= 0, heads >= 1, R = T*heads < 2^30, eps finite >= 0
  *   - rows do not overlap: heads == 1: stride_t >= H (or T <= 1);
  *     heads > 1: stride_h >= H and stride_t >= heads*stride_h (or T <= 1)
  *                                                         else RMSN_ERR_INVALID_ARG
@@ -69,8 +69,8 @@ enum rmsn_dtype { RMSN_W_BF16 = 0, RMSN_W_F32 = 1 };
 #define RMSN_MAX_H 16384
 
 /*
- * Forward (p1 #8577 opening paragraph: "The forward returns y (BF16) and rstd
- * (FP32)"; p1 #8577 "Key" for `res`, `w32` and the per-head views).
+ * Forward (p1 #8577 opening paragraph: its outputs are y in BF16 and rstd in
+ * FP32; p1 #8577 "Key" for `res`, `w32` and the per-head views).
  *   x            [T,heads,H] BF16 input.
  *   residual     [T,heads,H] BF16 r, or NULL.  With r, h = bf16(x + r) (sum in
  *                FP32, one round-to-nearest-even) is written to residual_out
@@ -82,7 +82,7 @@ enum rmsn_dtype { RMSN_W_BF16 = 0, RMSN_W_F32 = 1 };
  *   eps          added to the mean of squares (the pages measure eps = 1e-6).
  *   deterministic accepted for symmetry with the backward; the forward is
  *                the same program, bit for bit, in both modes (p1 #8577
- *                opening paragraph: the modes "use the same forward").
+ *                opening paragraph: both modes share one forward).
  */
 int rmsnorm_fwd(const void* x, const void* residual, const void* w, int w_dtype,
                 void* y, void* residual_out, float* rstd,
@@ -108,8 +108,8 @@ size_t rmsnorm_bwd_workspace_size(int64_t T, int64_t heads, int64_t H, int deter
 int rmsnorm_bwd_workspace_init(void* workspace, size_t workspace_bytes, int64_t H, void* stream);
 
 /*
- * Backward (p1 #8577 opening paragraph: "the backward returns dx (BF16) and
- * dw (FP32)"; p1 #8208 commit message for the deterministic flag).
+ * Backward (p1 #8577 opening paragraph: its outputs are dx in BF16 and dw in
+ * FP32; p1 #8208 commit message for the deterministic flag).
  *   dy        [T,heads,H] BF16 incoming gradient of y.
  *   x         [T,heads,H] BF16 normalised input of the forward (h when the
  *             forward had a residual).
@@ -125,8 +125,9 @@ int rmsnorm_bwd_workspace_init(void* workspace, size_t workspace_bytes, int64_t 
  *   deterministic 1: each chunk of rows writes FP64 column partials and a
  *             second kernel sums them in a fixed order, so dw is bitwise
  *             reproducible for a given shape on any MI355X.
- *             0: chunks add their FP64 partials atomically (or take the
- *             fixed-order pair where the route table finds it faster).
+ *             0: the route may add the chunks' FP64 partials atomically;
+ *             the measured MI355X route takes the fixed-order pair at every
+ *             shape, as it is faster there (rmsnorm_bwd_route reports it).
  */
 int rmsnorm_bwd(const void* dy, const void* x, const float* rstd, const void* w, int w_dtype,
                 const void* residual, void* dx, float* dw,
@@ -136,8 +137,8 @@ int rmsnorm_bwd(const void* dy, const void* x, const float* rstd, const void* w,
 
 /*
  * Route inspection and override, for the route-table measurement and for
- * tests that cover both sides of a route edge (p3 #8293 commit message: the
- * pairs test covers both sides of the edges).  A route names how the
+ * tests that cover both sides of a route edge (p3 #8293 commit message: its
+ * pairs test exercises each edge from both sides).  A route names how the
  * backward reduces dw over rows:
  *   form   RMSN_FORM_PAIR: each of `chunks` workgroups writes an FP64 column
  *          partial to the workspace and a second kernel sums them in a fixed

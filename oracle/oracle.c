@@ -23,8 +23,9 @@
  *    [p1 #8577 "Key" and "Baselines and measurement"].
  *  - Per-head views [T,heads,256] share one w[256]; the rows are T*heads and
  *    dw sums over all of them  [p1 #8577 "Key"].
- *  - dw is compared "against FP64 at the kernel's FP32 rstd"  [p1 #8208
- *    commit message], so the backward takes rstd as an input.
+ *  - dw is checked against an FP64 evaluation that uses the kernel's own
+ *    FP32 rstd  [p1 #8208 commit message], so the backward takes rstd as an
+ *    input.
  *
  * The pages never print the formula.  The plain reading used here (RMS over
  * the H entries, divide by H, eps inside the square root, no bias):
