@@ -16,7 +16,11 @@ using namespace rmsn;
 
 namespace {
 
+// R = T * heads must stay below 2^30 (row indices are 32-bit in the kernels,
+// with room for a whole grid's step beyond the last row).
 constexpr int64_t kMaxRows = int64_t(1) << 30;
+
+bool rows_ok(int64_t T, int64_t heads) { return T >= 0 && heads >= 1 && T <= (kMaxRows - 1) / heads; }
 
 bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
 
@@ -29,7 +33,7 @@ int check_shape(int64_t T, int64_t heads, int64_t H, int64_t st, int64_t sh, Sha
 {
     if (T < 0 || heads < 1 || H < 1) return RMSN_ERR_INVALID_ARG;
     if (H % 8 != 0 || H > RMSN_MAX_H) return RMSN_ERR_UNSUPPORTED;
-    if (T > kMaxRows / heads) return RMSN_ERR_INVALID_ARG;
+    if (!rows_ok(T, heads)) return RMSN_ERR_INVALID_ARG;
     const int64_t R = T * heads;
     if (st < 0 || sh < 0) return RMSN_ERR_INVALID_ARG;
     if (heads == 1) {
@@ -163,7 +167,7 @@ int rmsnorm_fwd(const void* x, const void* residual, const void* w, int w_dtype,
 size_t rmsnorm_bwd_workspace_size(int64_t T, int64_t heads, int64_t H, int deterministic)
 {
     (void)deterministic;  // one layout serves both modes
-    if (T < 0 || heads < 1 || H < 1 || H % 8 != 0 || H > RMSN_MAX_H || T > kMaxRows / heads) return 0;
+    if (!rows_ok(T, heads) || H < 1 || H % 8 != 0 || H > RMSN_MAX_H) return 0;
     const int64_t R = T * heads;
     size_t best = ws_part_offset(H);
     for (int det = 0; det <= 1; ++det)
@@ -177,7 +181,7 @@ size_t rmsnorm_bwd_workspace_size(int64_t T, int64_t heads, int64_t H, int deter
 
 size_t rmsnorm_bwd_workspace_size_for_route(int64_t T, int64_t heads, int64_t H, rmsn_route route)
 {
-    if (T < 0 || heads < 1 || H < 1 || H % 8 != 0 || H > RMSN_MAX_H || T > kMaxRows / heads) return 0;
+    if (!rows_ok(T, heads) || H < 1 || H % 8 != 0 || H > RMSN_MAX_H) return 0;
     if (route.chunks < 1 || route.chunks > kMaxChunks) return 0;
     if (route.form != RMSN_FORM_PAIR && route.form != RMSN_FORM_ATOMIC) return 0;
     return ws_bytes_for(T * heads, H, BwdRoute{route.form, route.chunks});
@@ -197,7 +201,7 @@ int rmsnorm_bwd_route(int64_t T, int64_t heads, int64_t H, int w_dtype, int has_
 {
     if (!out) return RMSN_ERR_INVALID_ARG;
     if (w_dtype != RMSN_W_BF16 && w_dtype != RMSN_W_F32) return RMSN_ERR_INVALID_ARG;
-    if (T < 0 || heads < 1 || H < 1 || T > kMaxRows / heads) return RMSN_ERR_INVALID_ARG;
+    if (!rows_ok(T, heads) || H < 1) return RMSN_ERR_INVALID_ARG;
     if (H % 8 != 0 || H > RMSN_MAX_H) return RMSN_ERR_UNSUPPORTED;
     const BwdRoute r = default_bwd_route(T * heads, H, w_dtype == RMSN_W_F32, has_residual != 0, deterministic != 0);
     out->form = r.form;

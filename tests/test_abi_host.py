@@ -172,3 +172,14 @@ def test_route_chunk_count_grows_with_rows_and_stays_bounded():
             prev = chunks
         assert rn.rmsnorm_bwd_route(1, 1, H, 0, 0, 1)[1] == 1
         assert prev >= 256
+
+
+def test_row_count_limit_is_below_2_pow_30():
+    r = rn.RmsnRoute()
+    L = rn.lib()
+    for heads in (1, 3, 24):
+        last = ((1 << 30) - 1) // heads  # largest T with T * heads < 2^30
+        assert L.rmsnorm_bwd_route(last, heads, 256, 0, 0, 1, ctypes.byref(r)) == rn.RMSN_OK
+        assert L.rmsnorm_bwd_route(last + 1, heads, 256, 0, 0, 1, ctypes.byref(r)) == rn.RMSN_ERR_INVALID_ARG
+        assert rn.rmsnorm_bwd_workspace_size(last, heads, 256) > 0
+        assert rn.rmsnorm_bwd_workspace_size(last + 1, heads, 256) == 0
