@@ -3,8 +3,9 @@
 //   xhat = u * rstd,  c = mean(xhat * w * dy)
 //   dx   = bf16(rstd * (w * dy - xhat * c) [+ dres])
 //   dw   = sum over rows of dy * xhat
-// (FlashInfer training-RMSNorm pages: p1 #8577 opening paragraph; dw is
-// compared against FP64 at the kernel's FP32 rstd, p1 #8208 commit message.)
+// (FlashInfer training-RMSNorm pages: p1 #8577 opening paragraph; the dw
+// reference is an FP64 evaluation that takes the kernel's FP32 rstd, p1
+// #8208 commit message.)
 //
 // Row kernel.  Workgroup c of `chunks` takes every chunks-th group of rows
 // (its "chunk"); a row group of LPR lanes owns a row, each lane V 16-byte
@@ -20,8 +21,9 @@
 //
 // dw.  Each lane keeps FP64 column sums over the chunk's rows in registers;
 // row groups of one workgroup are added by lane exchanges inside a
-// wavefront, then across wavefronts through LDS, in a fixed order.  With a single
-// chunk that sum is dw and is written directly; otherwise the chunk sum goes
+// wavefront, then across wavefronts through LDS, in a fixed order.  With a
+// single chunk that sum is dw and is written directly; otherwise the chunk
+// sum goes
 //   pair form:   to row `chunk` of a workspace [chunks, H] (FP64), summed by
 //                dw_reduce_kernel in a fixed order -- deterministic;
 //   atomic form: into an FP64 [H] accumulator by atomic add; the workgroup
@@ -30,7 +32,6 @@
 #include "device_common.h"
 #include "kernels.h"
 #include "route.h"
-
 
 namespace rmsn {
 

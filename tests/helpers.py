@@ -7,9 +7,9 @@ Tolerances (checked element by element):
   * y and dx: within 1 BF16 unit in the last place of the oracle's FP64 value
     rounded once to BF16 (dx evaluated at the kernel's FP32 rstd).
   * rstd: relative error <= 1e-6 against the oracle's FP64 rstd.
-  * dw: |dw - ref| <= 1e-4 + 1e-4 |ref| per element against FP64 at the
-    kernel's FP32 rstd (p1 #8577 "Baselines and measurement"; p1 #8208
-    commit message).
+  * dw: |dw - ref| <= 1e-4 + 1e-4 |ref| per element, ref being the FP64
+    value evaluated at the kernel's FP32 rstd (p1 #8577 "Baselines and
+    measurement"; p1 #8208 commit message).
 """
 from __future__ import annotations
 
