@@ -334,6 +334,80 @@ def shape_latencies(shapes, flush_buf, rounds, reps):
             "launches_per_op": rounds * reps, "rows": rows}
 
 
+# ---- kernel spans (the pages' latency: first kernel start to last kernel
+# end of one op after a cache flush, from the GPU's own timestamps) --------
+#
+# `--span-sweep SEQ` runs, for every shape, `reps` x [flush, op] per op and
+# writes the list of segment labels to SEQ; run it under
+#   rocprofv3 --kernel-trace --output-format csv -d OUT -o run -- python3 bench.py --span-sweep SEQ
+# and `--span-report TRACE SEQ` turns OUT/.../run_kernel_trace.csv into
+# per-shape medians.  Every segment starts with the flush (the only float
+# fill kernel); setup and warm-up kernels sit in segments labelled "skip".
+
+FLUSH_KERNEL = "FillFunctor<float>"
+
+
+def span_sweep(shapes, reps, seq_path):
+    import torch
+
+    flush = torch.empty(1 << 28, dtype=torch.float32, device="cuda")
+    labels = []
+
+    def mark(label):
+        flush.fill_(1)
+        labels.append(label)
+
+    mark("skip")
+    for H, T, wdt, res in shapes:
+        c = DeviceCase(H, T, wdt, res)
+        ops = {"fwd": c.fwd, "bwd_det": lambda: c.bwd(True), "bwd_nondet": lambda: c.bwd(False),
+               "step_det": c.step}
+        for fn in ops.values():
+            fn()
+        for name, fn in ops.items():
+            for _ in range(reps):
+                mark(f"{shape_name(H, T, wdt, res)}|{name}")
+                fn()
+        mark("skip")
+        torch.cuda.synchronize()
+        del c
+    with open(seq_path, "w") as f:
+        json.dump(labels, f)
+    return len(labels)
+
+
+def span_report(trace_csv, seq_path):
+    """Median kernel span (us) per shape and op from a rocprofv3 kernel trace."""
+    import csv
+
+    labels = json.load(open(seq_path))
+    rows = list(csv.DictReader(open(trace_csv)))
+    key = "Dispatch_Id" if rows and "Dispatch_Id" in rows[0] else "Start_Timestamp"
+    rows.sort(key=lambda r: int(r[key]))
+    segs = []
+    for r in rows:
+        if FLUSH_KERNEL in r["Kernel_Name"]:
+            segs.append([])
+        elif segs:
+            segs[-1].append((int(r["Start_Timestamp"]), int(r["End_Timestamp"]), r["Kernel_Name"]))
+    if len(segs) != len(labels):
+        raise SystemExit(f"{len(segs)} flush-delimited segments in the trace, {len(labels)} labels")
+    spans, kernels = {}, {}
+    for lab, seg in zip(labels, segs):
+        if lab == "skip":
+            continue
+        if not seg:
+            raise SystemExit(f"segment {lab} has no kernels")
+        spans.setdefault(lab, []).append((max(e for _, e, _ in seg) - min(b for b, _, _ in seg)) / 1e3)
+        kernels[lab] = len(seg)
+    out = {}
+    for lab, v in spans.items():
+        shape, op = lab.split("|")
+        out.setdefault(shape, {})[op] = {"median_us": round(statistics.median(v), 2), "n": len(v),
+                                         "kernels": kernels[lab]}
+    return out
+
+
 def _step_oracle(wl, rows):
     """One oracle step over the leading `rows` rows; seconds of its three ops."""
     import oracle
@@ -370,9 +444,19 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--profile", action="store_true",
                     help="only warmup + timed steps (for rocprofv3 runs), no per-op extras")
+    ap.add_argument("--span-sweep", metavar="SEQ",
+                    help="run the pages' shapes as flush-delimited ops for a rocprofv3 kernel trace; "
+                         "write the segment labels to SEQ and exit")
+    ap.add_argument("--span-report", nargs=2, metavar=("TRACE_CSV", "SEQ"),
+                    help="print per-shape median kernel spans from a --span-sweep trace and exit")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain 1 GiB device copy (reference for HBM counter scaling)")
     args = ap.parse_args()
+
+    if args.span_report:
+        rep = span_report(*args.span_report)
+        print(json.dumps({"kernel_spans_us": rep}))
+        return
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path "
@@ -388,6 +472,11 @@ def main():
     import rmsnorm_fwd_amd as rn
 
     rn.lib()  # fail loudly if the HIP library is not built
+    if args.span_sweep:
+        n = span_sweep(SWEEP_SHAPES, 20, args.span_sweep)
+        torch.cuda.synchronize()
+        log(f"span sweep: {n} flush-delimited segments, labels in {args.span_sweep}")
+        return
     if args.copy_calibration:
         # the first three device-to-device copies of the process: 1 GiB each
         src = torch.empty(1 << 29, dtype=torch.int16, device="cuda").fill_(3)
