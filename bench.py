@@ -309,10 +309,29 @@ class DeviceCase:
         self.bwd(True)
 
 
+def graphed(fn):
+    """fn captured once in a HIP graph (after an eager warm-up on the capture
+    stream); returns the replay function.  The library's calls allocate
+    nothing and never synchronise, so the whole op can be captured."""
+    import torch
+
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        fn()
+    torch.cuda.current_stream().wait_stream(s)
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=s):
+        fn()
+    torch.cuda.synchronize()
+    return g.replay
+
+
 def shape_latencies(shapes, flush_buf, rounds, reps):
     """Cache-flushed median latency (us) of fwd, bwd (both modes) and the
-    deterministic 2xfwd+bwd step for each shape, plus the floor: the same
-    timing around a one-element torch fill."""
+    deterministic 2xfwd+bwd step for each shape -- the backward and the step
+    also as one HIP-graph replay each (the pages time graph replays) -- plus
+    the floor: the same timing around a one-element torch fill."""
     import torch
 
     tiny = torch.empty(1, dtype=torch.float32, device="cuda")
@@ -324,6 +343,8 @@ def shape_latencies(shapes, flush_buf, rounds, reps):
                "step_det": c.step}
         for fn in ops.values():
             fn()
+        ops["bwd_det_graph"] = graphed(lambda: c.bwd(True))
+        ops["step_det_graph"] = graphed(c.step)
         raw = time_cold(ops, rounds, reps, flush_buf)
         row = {"shape": shape_name(H, T, wdt, res)}
         for k, v in raw.items():
@@ -537,6 +558,7 @@ def main():
             "step_det": (lambda: wl.step(True), wl.step_bytes),
             "step_nondet": (lambda: wl.step(False), wl.step_bytes),
         }
+        ops["step_det_graph"] = (graphed(lambda: wl.step(True)), wl.step_bytes)
         for fn, _ in ops.values():
             for _ in range(3):
                 fn()
