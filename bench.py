@@ -102,6 +102,9 @@ class Workload:
         self.x = self.view(place(self.x_h))
         self.dy = self.view(place(self.dy_h))
         self.r = self.view(place(self.r_h)) if res else None
+        # the incoming gradient of h for the residual backward's second form
+        # (dres ~ N(0,1)); the step itself takes dres = NULL
+        self.dres = self.view(place(synth.rows(seed, "dres", 0, self.R, H))) if res else None
         self.w = (torch.from_numpy(self.w_h).to(dev) if wdt == "f32" else
                   torch.from_numpy(self.w_h.view(np.int16)).view(torch.bfloat16).to(dev))
         self.y = self.view(place(self.x_h))
@@ -119,10 +122,10 @@ class Workload:
         self.rn.rmsnorm_fwd(self.x, self.w, EPS, residual=self.r, y=self.y, residual_out=self.h,
                             rstd=self.rstd)
 
-    def bwd(self, det=True):
+    def bwd(self, det=True, dres=None):
         u = self.h if self.res else self.x
-        self.rn.rmsnorm_bwd(self.dy, u, self.rstd, self.w, deterministic=det, dx=self.dx, dw=self.dw,
-                            workspace=self.ws)
+        self.rn.rmsnorm_bwd(self.dy, u, self.rstd, self.w, residual=dres, deterministic=det, dx=self.dx,
+                            dw=self.dw, workspace=self.ws)
 
     def step(self, det=True):
         self.fwd()
@@ -555,6 +558,8 @@ def main():
             "fwd_aa": (wl.fwd, wl.fwd_bytes),
             "bwd_det": (lambda: wl.bwd(True), wl.bwd_bytes),
             "bwd_nondet": (lambda: wl.bwd(False), wl.bwd_bytes),
+            **({"bwd_det_dres": (lambda: wl.bwd(True, wl.dres), bwd_bytes(wl.R, wl.H, wl.sw, True))}
+               if wl.res else {}),
             "step_det": (lambda: wl.step(True), wl.step_bytes),
             "step_nondet": (lambda: wl.step(False), wl.step_bytes),
         }

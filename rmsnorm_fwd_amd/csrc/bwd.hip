@@ -60,17 +60,19 @@ __device__ __forceinline__ double chunk_group_sum(const double* part, int chunks
     return s;
 }
 
-// One iteration's rows of a row group: addresses, rstd and the x / dy vectors.
-template <int U, int V>
+// One iteration's rows of a row group: addresses, rstd and the x / dy (and
+// dres) vectors, all loaded before any of them is used.
+template <int U, int V, bool DRES>
 struct BwdTile {
     bool ok[U];
     int64_t off[U];
     double rho[U];
     uint4 xv[U][V], dv[U][V];
+    uint4 rv[DRES ? U : 1][DRES ? V : 1];
 };
 
-template <int U, int V, int SLOTS>
-__device__ __forceinline__ void bwd_load(BwdTile<U, V>& t, const BwdParams& p, const LaneVectors<V>& lv,
+template <int U, int V, int SLOTS, bool DRES>
+__device__ __forceinline__ void bwd_load(BwdTile<U, V, DRES>& t, const BwdParams& p, const LaneVectors<V>& lv,
                                          int base, int slot, int row1)
 {
 #pragma unroll
@@ -87,6 +89,7 @@ __device__ __forceinline__ void bwd_load(BwdTile<U, V>& t, const BwdParams& p, c
         for (int v = 0; v < V; ++v) {
             t.xv[u][v] = ld16_stream(p.x + t.off[u] + lv.col[v]);
             t.dv[u][v] = ld16_stream(p.dy + t.off[u] + lv.col[v]);
+            if constexpr (DRES) t.rv[u][v] = ld16_stream(p.dres + t.off[u] + lv.col[v]);
         }
 }
 
@@ -137,10 +140,10 @@ __global__ void __launch_bounds__(block_of(LPR)) bwd_kernel(BwdParams p)
 #pragma unroll
         for (int e = 0; e < 8; ++e) acc[v][e] = 0.0;
 
-    BwdTile<U, V> cur;
+    BwdTile<U, V, DRES> cur;
     int it = 0;
     for (int base = first; base < row1; base += step, ++it) {
-        bwd_load<U, V, SLOTS>(cur, p, lv, base, slot, row1);
+        bwd_load<U, V, SLOTS, DRES>(cur, p, lv, base, slot, row1);
         const bool* ok = cur.ok;
         const int64_t* off = cur.off;
         const double* rho = cur.rho;
@@ -172,7 +175,7 @@ __global__ void __launch_bounds__(block_of(LPR)) bwd_kernel(BwdParams p)
                 float xf[8], df[8], rf[8];
                 unpack8(xv[u][v], xf);
                 unpack8(dv[u][v], df);
-                if constexpr (DRES) unpack8(ld16(p.dres + off[u] + lv.col[v]), rf);
+                if constexpr (DRES) unpack8(cur.rv[u][v], rf);
                 double d[8];
 #pragma unroll
                 for (int e = 0; e < 8; ++e) {
