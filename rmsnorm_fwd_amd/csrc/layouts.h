@@ -43,7 +43,7 @@ struct Layout {
     X(7, 3072, 64, 6, 1, 32)   \
     X(8, 4096, 512, 1, 2, 32)  \
     X(9, 5120, 320, 2, 2, 32)  \
-    X(10, 6144, 768, 1, 2, 16) \
+    X(10, 6144, 768, 1, 2, 24) \
     X(11, 8192, 512, 2, 2, 32) \
     X(12, 16384, 512, 4, 1, 8)
 
