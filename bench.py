@@ -532,7 +532,7 @@ def main():
     log(f"timed {args.steps} steps: {ms_per_step * 1e3:.1f} us/step, {value:.0f} GB/s (wall {wall:.3f}s)")
 
     out = {
-        "metric": "RMSNorm fwd/bwd/2xfwd+bwd us and effective HBM GB/s (% of peak) at [T,H]",
+        "metric": "RMSNorm fwd/bwd/2xfwd+bwd \u00b5s and effective HBM GB/s (% of peak) at [T,H]",
         "value": round(value, 1),
         "unit": "GB/s",
         "n_gpus": 1,
