@@ -579,6 +579,8 @@ def main():
             log(f"cold {name}: {c['median_us']:.1f} us  {c['gbs']:.0f} GB/s ({c['pct_peak']:.1f}%)")
         lat["aa_floor_pct"] = round(100 * abs(lat["fwd"]["median_us"] - lat["fwd_aa"]["median_us"])
                                     / lat["fwd"]["median_us"], 3)
+        # deterministic over non-deterministic backward time (> 1: non-det faster)
+        lat["mode_ratio_bwd"] = round(lat["bwd_det"]["median_us"] / lat["bwd_nondet"]["median_us"], 4)
         out["latency_cold"] = lat
 
         if not args.no_small_t:
