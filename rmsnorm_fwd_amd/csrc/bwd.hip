@@ -315,11 +315,32 @@ static hipError_t bwd_dispatch(bool w_f32, const BwdParams& p, hipStream_t s)
     return w_f32 ? bwd_t<LPR, V, U, true, false>(p, s) : bwd_t<LPR, V, U, false, false>(p, s);
 }
 
+// Single-workgroup path: the smallest U in {1, 2, 4} (up to direct_max_u)
+// whose one iteration covers every row.
+template <int LPR, int V, int U>
+static hipError_t bwd_direct(bool w_f32, const BwdParams& p, hipStream_t s)
+{
+    constexpr int UMAX = direct_max_u(LPR, V, U);
+    constexpr int SL = slots_of(LPR);
+    if constexpr (UMAX >= 2 && U < UMAX) {
+        if (p.R <= SL) return bwd_dispatch<LPR, V, 1>(w_f32, p, s);
+        if constexpr (UMAX >= 4)
+            if (p.R > 2 * SL) return bwd_dispatch<LPR, V, 4>(w_f32, p, s);
+        return bwd_dispatch<LPR, V, 2>(w_f32, p, s);
+    } else if constexpr (UMAX >= 2) {
+        if (p.R <= SL) return bwd_dispatch<LPR, V, 1>(w_f32, p, s);
+        return bwd_dispatch<LPR, V, UMAX>(w_f32, p, s);
+    } else {
+        return bwd_dispatch<LPR, V, U>(w_f32, p, s);
+    }
+}
+
 hipError_t launch_bwd(int layout, bool w_f32, const BwdParams& p, hipStream_t s)
 {
     switch (layout) {
-#define RMSN_BWD_CASE(id, mh, l, vv, uu, kk) \
-    case id: return bwd_dispatch<l, vv, uu>(w_f32, p, s);
+#define RMSN_BWD_CASE(id, mh, l, vv, uu, kk)                                                 \
+    case id:                                                                                 \
+        return p.direct_dw ? bwd_direct<l, vv, uu>(w_f32, p, s) : bwd_dispatch<l, vv, uu>(w_f32, p, s);
         RMSN_BWD_LAYOUTS(RMSN_BWD_CASE)
 #undef RMSN_BWD_CASE
     default: return hipErrorInvalidValue;

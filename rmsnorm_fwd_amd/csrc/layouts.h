@@ -91,6 +91,21 @@ static constexpr int kNumBwdLayouts = sizeof(kBwdLayouts) / sizeof(kBwdLayouts[0
 constexpr int block_of(int lpr) { return lpr >= 256 ? lpr : lpr * (256 / lpr); }
 constexpr int slots_of(int lpr) { return block_of(lpr) / lpr; }
 
+// The backward's single-workgroup path (small T: one workgroup takes every
+// row and writes dw itself) runs with the fewest rows per row group and
+// iteration (U = 1, 2 or 4) that covers all rows in one iteration: measured
+// at T 1-16, each extra iteration costs 1.3-2.5 us of cold loads in series,
+// while a larger U costs 0.4-1.5 us even when its rows are not needed.
+// Lanes and vectors per row stay the layout's, so every per-row sum -- and
+// dx -- is the one of the multi-workgroup path.  Largest U: 4 for rows of up
+// to 2 vectors per lane, 2 for 3; rows spanning more than 256 lanes keep
+// the layout's U (their workgroups are too large for more registers).
+#ifdef RMSN_DIRECT_U_AS_LAYOUT  // tuning builds: only the table's U
+constexpr int direct_max_u(int, int, int u) { return u; }
+#else
+constexpr int direct_max_u(int lpr, int v, int u) { return lpr > 256 ? u : (v <= 2 ? 4 : (v == 3 ? 2 : u)); }
+#endif
+
 // Smallest layout that covers H (tables are sorted by max_h); -1 if none.
 inline int pick_layout(const Layout* t, int n, long long H)
 {

@@ -11,12 +11,12 @@
 
 namespace rmsn {
 
-int bwd_rows_per_iter(int64_t H)
+int bwd_direct_rows_per_iter(int64_t H)
 {
     const int id = pick_layout(kBwdLayouts, kNumBwdLayouts, H);
     if (id < 0) return 0;
     const Layout& L = kBwdLayouts[id];
-    return slots_of(L.lpr) * L.u;
+    return slots_of(L.lpr) * direct_max_u(L.lpr, L.v, L.u);
 }
 
 size_t ws_bytes_for(int64_t R, int64_t H, const BwdRoute& r)
@@ -55,10 +55,13 @@ BwdRoute default_bwd_route(int64_t R, int64_t H, bool w_f32, bool residual, bool
     if (c < 128) c = groups < 128 ? groups : 128;
     if (c > L.k) c = L.k;
     r.chunks = (int)(c > 0 ? c : 1);
-    // Up to two row groups one workgroup does all the rows and writes dw
-    // itself, which saves the reduce launch (measured at T 1 to 256, H 256
-    // to 6144: 1.5-3 us faster than two workgroups plus the reduce).
-    if (groups <= 2) r.chunks = 1;
+    // When one iteration of a single workgroup covers every row (it may take
+    // more rows per iteration than the multi-workgroup layout, see
+    // direct_max_u), that workgroup writes dw itself and the reduce launch
+    // goes: measured at T 1-128, H 256-6144, 0.5-2 us faster than the pair
+    // with one row group per workgroup; one more iteration already costs
+    // 1.3-4 us (cold loads in series), more than the reduce launch.
+    if (groups <= 2 || R <= (int64_t)bwd_direct_rows_per_iter(H)) r.chunks = 1;
     return r;
 }
 

@@ -30,8 +30,9 @@ size_t ws_bytes_for(int64_t R, int64_t H, const BwdRoute& r);
 // The measured route table (route.cpp).
 BwdRoute default_bwd_route(int64_t R, int64_t H, bool w_f32, bool residual, bool deterministic);
 
-// Rows one iteration of the backward row kernel covers for this width.
-int bwd_rows_per_iter(int64_t H);
+// Rows one iteration covers when a single workgroup does every row (chunks
+// = 1, dw written directly) for this width.
+int bwd_direct_rows_per_iter(int64_t H);
 
 // Largest chunk count a route may ask for.
 constexpr int64_t kMaxChunks = 1 << 16;
