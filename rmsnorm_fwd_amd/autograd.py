@@ -31,12 +31,27 @@ def _like_layout(t, ref):
     return out
 
 
+def _rows(t):
+    """t as the library sees it: [T,H] or [T,heads,H] pass through; more
+    leading dimensions are folded into rows (a view when the strides allow
+    it, else a contiguous copy)."""
+    if t is None or t.dim() <= 3:
+        return t
+    try:
+        return t.view(-1, t.shape[-1])
+    except RuntimeError:
+        return t.reshape(-1, t.shape[-1])
+
+
 class RMSNormFunction(torch.autograd.Function):
     """y = RMSNorm(x [+ residual]) * w.  Returns y, or (y, h) with a residual,
-    where h = x + residual is the BF16 residual stream."""
+    where h = x + residual is the BF16 residual stream.  x may have any number
+    of leading dimensions; the last one is H."""
 
     @staticmethod
     def forward(ctx, x, w, residual, eps, deterministic, recompute):
+        ctx.shape = x.shape
+        x, residual = _rows(x), _rows(residual)
         ctx.set_materialize_grads(False)
         y, rstd, h = rmsnorm_fwd(x, w, eps, residual=residual, deterministic=deterministic)
         ctx.eps, ctx.deterministic, ctx.recompute = eps, deterministic, recompute
@@ -46,11 +61,12 @@ class RMSNormFunction(torch.autograd.Function):
         else:
             ctx.save_for_backward(h if residual is not None else x, w, rstd)
         if residual is not None:
-            return y, h
-        return y
+            return y.view(ctx.shape), h.view(ctx.shape)
+        return y.view(ctx.shape)
 
     @staticmethod
     def backward(ctx, dy, dh=None):
+        dy, dh = _rows(dy), _rows(dh)
         if ctx.recompute:
             x, w, residual = ctx.saved_tensors
             _, rstd, h = rmsnorm_fwd(x, w, ctx.eps, residual=residual, deterministic=ctx.deterministic)
@@ -63,6 +79,7 @@ class RMSNormFunction(torch.autograd.Function):
         dres = _like_layout(dh, u) if ctx.has_residual and dh is not None else None
         dx, dw = rmsnorm_bwd(dy, u, rstd, w, residual=dres, deterministic=ctx.deterministic)
         grad_w = dw if w.dtype == torch.float32 else dw.to(w.dtype)
+        dx = dx.view(ctx.shape)
         grad_res = dx if ctx.has_residual else None
         return dx, grad_w, grad_res, None, None, None
 

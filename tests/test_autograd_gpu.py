@@ -90,3 +90,38 @@ def test_module_and_views():
     got = to_host_bits(buf.grad.view(T, 8, H)[:, :heads].reshape(T * heads, H))
     assert ulp_dist(got, ref_dx).max() <= 1
     assert int(buf.grad.view(T, 8, H)[:, heads:].count_nonzero()) == 0
+
+
+@pytest.mark.parametrize("res", [False, True])
+def test_leading_dims_fold_into_rows(res):
+    # [B, S, N, H] inputs (contiguous, and a permuted one that needs a copy)
+    # give bitwise the outputs and gradients of the same rows as [R, H]
+    from rmsnorm_fwd_amd.autograd import rmsnorm
+    B, S, N, H = 2, 3, 11, 1536
+    R = B * S * N
+    x_h = synth.rows(9, "x", 0, R, H)
+    r_h = synth.rows(9, "r", 0, R, H)
+    g_h = synth.rows(9, "dy", 0, R, H)
+    w_h = synth.weight(9, H, "f32")
+
+    def run(shape_fn, unshape_fn):
+        x = shape_fn(to_dev_bf16(x_h).view(R, H)).detach().requires_grad_(True)
+        r = shape_fn(to_dev_bf16(r_h).view(R, H)).detach() if res else None
+        w = weight_dev(w_h).requires_grad_(True)
+        out = rmsnorm(x, w, EPS, residual=r)
+        y = out[0] if res else out
+        loss = (y.float() * shape_fn(to_dev_bf16(g_h).view(R, H)).float()).sum()
+        if res:
+            loss = loss + out[1].float().sum()
+        loss.backward()
+        return unshape_fn(y.detach()), unshape_fn(x.grad), w.grad
+
+    flat = run(lambda t: t, lambda t: t)
+    four = run(lambda t: t.view(B, S, N, H), lambda t: t.reshape(R, H))
+    perm = run(lambda t: t.view(S, B, N, H).permute(1, 0, 2, 3),
+               lambda t: t.permute(1, 0, 2, 3).reshape(R, H))
+    for other in (four, perm):
+        for a, b in zip(flat[:2], other[:2]):
+            assert torch.equal(a, b)
+    assert torch.equal(flat[2], four[2])
+    torch.testing.assert_close(flat[2], perm[2], rtol=1e-5, atol=1e-5)  # rows in another order
