@@ -204,3 +204,39 @@ def test_max_rows_periodic():
         check_dw(dw.cpu().numpy(), ref_dw, rep)
         del dx
     print(rep)
+
+
+def test_two_streams_with_own_workspaces():
+    # the library keeps no state between calls: two streams, each with its
+    # own workspace, running forward and backward at the same time give
+    # bitwise the results of running them one after the other
+    import torch
+    import rmsnorm_fwd_amd as rn
+    from tests.helpers import EPS, to_dev_bf16, weight_dev
+    import synth
+    cases = []
+    for k, (T, H) in enumerate(((3000, 4096), (5000, 1536))):
+        x = to_dev_bf16(synth.rows(60 + k, "x", 0, T, H)).view(T, H)
+        dy = to_dev_bf16(synth.rows(60 + k, "dy", 0, T, H)).view(T, H)
+        w = weight_dev(synth.weight(60 + k, H, "bf16"))
+        cases.append((x, dy, w, rn.rmsnorm_bwd_workspace(T, 1, H, "cuda")))
+
+    def run(c, stream):
+        x, dy, w, ws = c
+        with torch.cuda.stream(stream):
+            y, rstd, _ = rn.rmsnorm_fwd(x, w, EPS)
+            dx, dw = rn.rmsnorm_bwd(dy, x, rstd, w, workspace=ws)
+        return y, rstd, dx, dw
+
+    s0 = torch.cuda.current_stream()
+    ref = [run(c, s0) for c in cases]
+    torch.cuda.synchronize()
+    streams = [torch.cuda.Stream(), torch.cuda.Stream()]
+    for _ in range(3):
+        for s in streams:
+            s.wait_stream(s0)
+        got = [run(c, s) for c, s in zip(cases, streams)]
+        torch.cuda.synchronize()
+        for a, b in zip(ref, got):
+            for t, u in zip(a, b):
+                assert torch.equal(t, u)
