@@ -58,6 +58,16 @@ def _load():
     lib.oracle_bwd_bf16.restype = ctypes.c_int
     lib.oracle_dw_bf16.argtypes = [_i64, _i64, _ptr, _ptr, _ptr, _ptr]
     lib.oracle_dw_bf16.restype = None
+    lib.oracle_gated_fwd_f64.argtypes = [_i64, _i64, _ptr, _ptr, _ptr, ctypes.c_double, _ptr, _ptr]
+    lib.oracle_gated_fwd_f64.restype = None
+    lib.oracle_gated_bwd_f64.argtypes = [_i64, _i64, _ptr, _ptr, _ptr, _ptr, _ptr, _ptr, _ptr, _ptr]
+    lib.oracle_gated_bwd_f64.restype = None
+    lib.oracle_gated_fwd_bf16.argtypes = [_i64, _i64, _ptr, _ptr, _ptr, ctypes.c_int, ctypes.c_double,
+                                          _ptr, _ptr]
+    lib.oracle_gated_fwd_bf16.restype = ctypes.c_int
+    lib.oracle_gated_bwd_bf16.argtypes = [_i64, _i64, _ptr, _ptr, _ptr, _ptr, ctypes.c_int, _ptr,
+                                          _ptr, _ptr, _ptr, _ptr, _ptr]
+    lib.oracle_gated_bwd_bf16.restype = ctypes.c_int
     lib.oracle_num_threads.argtypes = []
     lib.oracle_num_threads.restype = ctypes.c_int
     _lib = lib
@@ -190,3 +200,62 @@ def dw_bf16(u: np.ndarray, dy: np.ndarray, rho32: np.ndarray) -> np.ndarray:
     dw = np.empty(H, dtype=np.float64)
     _load().oracle_dw_bf16(R, H, _p(u), _p(dy), _p(rho32), _p(dw))
     return dw
+
+
+# --------------------------------------------------------- SiLU-gated ----
+
+def gated_fwd_f64(u, g, w, eps):
+    """Gated y and rstd of FP64 rows u[R,H] with gate g[R,H] and weight w[H]."""
+    u, g, w = _c(u, np.float64), _c(g, np.float64), _c(w, np.float64)
+    R, H = u.shape
+    y = np.empty_like(u)
+    rstd = np.empty(R, dtype=np.float64)
+    _load().oracle_gated_fwd_f64(R, H, _p(u), _p(g), _p(w), float(eps), _p(y), _p(rstd))
+    return y, rstd
+
+
+def gated_bwd_f64(u, g, dy, w, rho):
+    """Gated dx, dg and dw of FP64 rows at the per-row rho."""
+    u, g, dy = _c(u, np.float64), _c(g, np.float64), _c(dy, np.float64)
+    w, rho = _c(w, np.float64), _c(rho, np.float64)
+    R, H = u.shape
+    dx, dg = np.empty_like(u), np.empty_like(u)
+    dw = np.empty(H, dtype=np.float64)
+    _load().oracle_gated_bwd_f64(R, H, _p(u), _p(g), _p(dy), _p(w), _p(rho), _p(dx), _p(dg), _p(dw))
+    return dx, dg, dw
+
+
+def gated_fwd_bf16(x: np.ndarray, g: np.ndarray, w: np.ndarray, eps: float):
+    """Gated forward from BF16 rows x, gate g: (y bf16 bits, rstd float64)."""
+    x = _c(x, np.uint16)
+    g = _c(g, np.uint16)
+    w, w32 = _weight(w)
+    R, H = x.shape
+    y = np.empty_like(x)
+    rstd = np.empty(R, dtype=np.float64)
+    rc = _load().oracle_gated_fwd_bf16(R, H, _p(x), _p(g), _p(w), w32, float(eps), _p(y), _p(rstd))
+    if rc != 0:
+        raise RuntimeError(f"oracle_gated_fwd_bf16 failed ({rc})")
+    return y, rstd
+
+
+def gated_bwd_bf16(u: np.ndarray, g: np.ndarray, dy: np.ndarray, w: np.ndarray, rho32: np.ndarray,
+                   want_f64: bool = False):
+    """Gated backward at the kernel's FP32 rstd.
+
+    Returns (dx bits, dg bits, dx64 or None, dg64 or None, dw float64)."""
+    u = _c(u, np.uint16)
+    g = _c(g, np.uint16)
+    dy = _c(dy, np.uint16)
+    rho32 = _c(rho32, np.float32)
+    w, w32 = _weight(w)
+    R, H = u.shape
+    dx, dg = np.empty_like(u), np.empty_like(u)
+    dx64 = np.empty(u.shape, dtype=np.float64) if want_f64 else None
+    dg64 = np.empty(u.shape, dtype=np.float64) if want_f64 else None
+    dw = np.empty(H, dtype=np.float64)
+    rc = _load().oracle_gated_bwd_bf16(R, H, _p(u), _p(g), _p(dy), _p(w), w32, _p(rho32), _p(dx), _p(dg),
+                                       _p(dx64), _p(dg64), _p(dw))
+    if rc != 0:
+        raise RuntimeError(f"oracle_gated_bwd_bf16 failed ({rc})")
+    return dx, dg, dx64, dg64, dw

@@ -299,6 +299,179 @@ void oracle_dw_bf16(int64_t R, int64_t H, const uint16_t* u16, const uint16_t* d
     }
 }
 
+/* ---------------------------------------------------------------------- */
+/* SiLU-gated variant                                                      */
+/* ---------------------------------------------------------------------- */
+/* The pages name a SiLU-gated training RMSNorm next to this one (p1 #8208
+ * PR description: the kernel's other variants, deterministic and not) but
+ * never state its formula.  Reading taken (the common gated-RMSNorm form,
+ * gate applied to the normalised, weighted output; the gate does not enter
+ * the norm):
+ *    y_j  = u_j * rstd * w_j * silu(g_j),   silu(g) = g * sigmoid(g)
+ * and for L = sum_j dy_j * y_j, with a_j = xhat_j * w_j (xhat = u * rho):
+ *    dg_j = dy_j * a_j * silu'(g_j),  silu'(g) = s(g) * (1 + g * (1 - s(g))),
+ *           s = sigmoid
+ *    and dx, dw are the plain backward's at the gated gradient
+ *    e_j = dy_j * silu(g_j):
+ *    dx_j = rho * (w_j * e_j - xhat_j * c),  c = (1/H) sum_j xhat_j * w_j * e_j
+ *    dw_j = sum over rows of e_j * xhat_j
+ * The tests pin all three with central finite differences. */
+
+static double sigmoid(double g) { return 1.0 / (1.0 + exp(-g)); }
+static double silu(double g) { return g * sigmoid(g); }
+static double silu_grad(double g)
+{
+    const double sg = sigmoid(g);
+    return sg * (1.0 + g * (1.0 - sg));
+}
+
+/* One row of the gated backward at rho: dx and dg (dw is summed by the
+ * callers over rows).  e = dy * silu(g) is the gradient reaching the plain
+ * normalised output; e is left in the caller's buffer. */
+static void gated_row_bwd(int64_t H, const double* u, const double* g, const double* dy,
+                          const double* w, double rho, double* e, double* dx, double* dg)
+{
+    for (int64_t j = 0; j < H; ++j) {
+        e[j] = dy[j] * silu(g[j]);
+        dg[j] = dy[j] * ((u[j] * rho) * w[j]) * silu_grad(g[j]);
+    }
+    row_dx(H, u, e, w, rho, NULL, dx);
+}
+
+/* Gated forward on FP64 rows. */
+void oracle_gated_fwd_f64(int64_t R, int64_t H, const double* u, const double* g,
+                          const double* w, double eps, double* y, double* rstd)
+{
+#pragma omp parallel for schedule(static)
+    for (int64_t r = 0; r < R; ++r) {
+        const double* ur = u + r * H;
+        double s = row_rstd(H, ur, eps);
+        rstd[r] = s;
+        for (int64_t j = 0; j < H; ++j) y[r * H + j] = ur[j] * s * w[j] * silu(g[r * H + j]);
+    }
+}
+
+/* Gated backward on FP64 rows at the per-row rho. */
+void oracle_gated_bwd_f64(int64_t R, int64_t H, const double* u, const double* g,
+                          const double* dy, const double* w, const double* rho,
+                          double* dx, double* dg, double* dw)
+{
+    int failed = 0;
+#pragma omp parallel
+    {
+        double* e = (double*)malloc((size_t)H * sizeof(double));
+        if (!e) {
+#pragma omp atomic write
+            failed = 1;
+        }
+#pragma omp for schedule(static)
+        for (int64_t r = 0; r < R; ++r) {
+            if (!e) continue;
+            gated_row_bwd(H, u + r * H, g + r * H, dy + r * H, w, rho[r], e, dx + r * H, dg + r * H);
+        }
+        free(e);
+    }
+    (void)failed;
+#pragma omp parallel for schedule(static)
+    for (int64_t j = 0; j < H; ++j) {
+        double acc = 0.0;
+        for (int64_t r = 0; r < R; ++r)
+            acc += (dy[r * H + j] * silu(g[r * H + j])) * (u[r * H + j] * rho[r]);
+        dw[j] = acc;
+    }
+}
+
+/* Forward from BF16 storage: y (BF16, one rounding) and rstd (FP64). */
+int oracle_gated_fwd_bf16(int64_t R, int64_t H, const uint16_t* x, const uint16_t* g,
+                          const void* w, int w_is_f32, double eps, uint16_t* y, double* rstd)
+{
+    if (R < 0 || H <= 0) return 1;
+    double* wd = (double*)malloc((size_t)H * sizeof(double));
+    if (!wd) return 2;
+    for (int64_t j = 0; j < H; ++j) wd[j] = weight_at(w, w_is_f32, j);
+    int failed = 0;
+#pragma omp parallel
+    {
+        double* u = (double*)malloc((size_t)H * sizeof(double));
+        if (!u) {
+#pragma omp atomic write
+            failed = 1;
+        }
+#pragma omp for schedule(static)
+        for (int64_t row = 0; row < R; ++row) {
+            if (!u) continue;
+            const int64_t o = row * H;
+            for (int64_t j = 0; j < H; ++j) u[j] = oracle_bf16_to_double(x[o + j]);
+            double s = row_rstd(H, u, eps);
+            rstd[row] = s;
+            for (int64_t j = 0; j < H; ++j)
+                y[o + j] = oracle_bf16_round(u[j] * s * wd[j] * silu(oracle_bf16_to_double(g[o + j])));
+        }
+        free(u);
+    }
+    free(wd);
+    return failed ? 2 : 0;
+}
+
+/* Backward from BF16 storage at the kernel's FP32 rstd: dx and dg as BF16
+ * (one rounding each; the FP64 values go to dx64 / dg64 when non-NULL) and
+ * dw in double, each column summed over the rows in row order. */
+int oracle_gated_bwd_bf16(int64_t R, int64_t H, const uint16_t* u16, const uint16_t* g16,
+                          const uint16_t* dy16, const void* w, int w_is_f32, const float* rho32,
+                          uint16_t* dx, uint16_t* dg, double* dx64, double* dg64, double* dw)
+{
+    if (R < 0 || H <= 0) return 1;
+    double* wd = (double*)malloc((size_t)H * sizeof(double));
+    if (!wd) return 2;
+    for (int64_t j = 0; j < H; ++j) wd[j] = weight_at(w, w_is_f32, j);
+    int failed = 0;
+#pragma omp parallel
+    {
+        double* buf = (double*)malloc((size_t)H * 6 * sizeof(double));
+        if (!buf) {
+#pragma omp atomic write
+            failed = 1;
+        }
+#pragma omp for schedule(static)
+        for (int64_t row = 0; row < R; ++row) {
+            if (!buf) continue;
+            double *u = buf, *gg = buf + H, *d = buf + 2 * H, *e = buf + 3 * H;
+            double *ox = buf + 4 * H, *og = buf + 5 * H;
+            const int64_t o = row * H;
+            for (int64_t j = 0; j < H; ++j) {
+                u[j] = oracle_bf16_to_double(u16[o + j]);
+                gg[j] = oracle_bf16_to_double(g16[o + j]);
+                d[j] = oracle_bf16_to_double(dy16[o + j]);
+            }
+            gated_row_bwd(H, u, gg, d, wd, (double)rho32[row], e, ox, og);
+            for (int64_t j = 0; j < H; ++j) {
+                dx[o + j] = oracle_bf16_round(ox[j]);
+                dg[o + j] = oracle_bf16_round(og[j]);
+                if (dx64) dx64[o + j] = ox[j];
+                if (dg64) dg64[o + j] = og[j];
+            }
+        }
+        free(buf);
+    }
+#pragma omp parallel for schedule(static)
+    for (int64_t j0 = 0; j0 < H; j0 += 64) {
+        int64_t j1 = j0 + 64 < H ? j0 + 64 : H;
+        double acc[64];
+        for (int64_t j = j0; j < j1; ++j) acc[j - j0] = 0.0;
+        for (int64_t row = 0; row < R; ++row) {
+            const double rho = (double)rho32[row];
+            for (int64_t j = j0; j < j1; ++j) {
+                const double e = oracle_bf16_to_double(dy16[row * H + j]) *
+                                 silu(oracle_bf16_to_double(g16[row * H + j]));
+                acc[j - j0] += e * (oracle_bf16_to_double(u16[row * H + j]) * rho);
+            }
+        }
+        for (int64_t j = j0; j < j1; ++j) dw[j] = acc[j - j0];
+    }
+    free(wd);
+    return failed ? 2 : 0;
+}
+
 int oracle_num_threads(void)
 {
     int n = 1;

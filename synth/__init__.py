@@ -29,7 +29,7 @@ import numpy as np
 
 ROW_BLOCK = 512
 
-TENSOR_IDS = {"x": 1, "r": 2, "dy": 3, "w": 4, "dres": 5}
+TENSOR_IDS = {"x": 1, "r": 2, "dy": 3, "w": 4, "dres": 5, "g": 6}
 FAMILIES = ("normal", "outlier", "offset")
 
 

@@ -35,6 +35,19 @@ MUTANTS = {
     "residual_sign": ("h[i] = oracle_bf16_round(oracle_bf16_to_double(x[i]) + oracle_bf16_to_double(r[i]));",
                       "h[i] = oracle_bf16_round(oracle_bf16_to_double(x[i]) - oracle_bf16_to_double(r[i]));"),
     "residual_not_normalised": ("u[j] = oracle_bf16_to_double(hb);", "u[j] = oracle_bf16_to_double(x[o + j]);"),
+    # SiLU-gated variant
+    "gate_dropped_f64_fwd": ("ur[j] * s * w[j] * silu(g[r * H + j])", "ur[j] * s * w[j]"),
+    "gate_dropped_bf16_fwd": ("u[j] * s * wd[j] * silu(oracle_bf16_to_double(g[o + j]))", "u[j] * s * wd[j]"),
+    "silu_is_identity": ("static double silu(double g) { return g * sigmoid(g); }",
+                         "static double silu(double g) { return g; }"),
+    "silu_grad_sign": ("return sg * (1.0 + g * (1.0 - sg));", "return sg * (1.0 - g * (1.0 - sg));"),
+    "silu_grad_without_sigmoid": ("return sg * (1.0 + g * (1.0 - sg));", "return (1.0 + g * (1.0 - sg));"),
+    "dg_without_w": ("dg[j] = dy[j] * ((u[j] * rho) * w[j]) * silu_grad(g[j]);",
+                     "dg[j] = dy[j] * (u[j] * rho) * silu_grad(g[j]);"),
+    "gated_dx_without_gate": ("e[j] = dy[j] * silu(g[j]);", "e[j] = dy[j];"),
+    "gated_dw_f64_without_gate": ("acc += (dy[r * H + j] * silu(g[r * H + j])) * (u[r * H + j] * rho[r]);",
+                                  "acc += dy[r * H + j] * (u[r * H + j] * rho[r]);"),
+    "gated_dw_bf16_without_gate": ("silu(oracle_bf16_to_double(g16[row * H + j]));", "1.0;"),
 }
 
 
@@ -48,6 +61,7 @@ def test_pins_catch_mutant(name, tmp_path):
     lib = obuild.build(src=str(path), lib=str(tmp_path / "liboracle_mutant.so"))
     env = dict(os.environ, RMSNORM_ORACLE_LIB=lib)
     proc = subprocess.run([sys.executable, "-m", "pytest", "-x", "-q", "-p", "no:cacheprovider",
-                           os.path.join(ROOT, "tests", "test_oracle_pins.py")],
+                           os.path.join(ROOT, "tests", "test_oracle_pins.py"),
+                           os.path.join(ROOT, "tests", "test_oracle_gated_pins.py")],
                           cwd=ROOT, env=env, capture_output=True, text=True, timeout=300)
     assert proc.returncode != 0, f"mutant {name} passed every pin:\n{proc.stdout[-2000:]}"
