@@ -50,16 +50,18 @@ WORKLOADS = {
     "T19968_H5120": (19968, 1, 5120, 5120, 5120, "bf16", False),
     "T6144_H5120": (6144, 1, 5120, 5120, 5120, "bf16", False),
     "T2048_H5120": (2048, 1, 5120, 5120, 5120, "bf16", False),
+    # the SiLU-gated variant (y = RMSNorm(x) * w * silu(g)) at the headline shape
+    "T65536_H4096_w32_gate": (65536, 1, 4096, 4096, 4096, "f32", "gate"),
 }
 DEFAULT_WORKLOAD = "T65536_H4096_w32"
 
 
-def fwd_bytes(R, H, sw, res):
-    return (8 if res else 4) * R * H + 4 * R + sw * H
+def fwd_bytes(R, H, sw, res, gate=False):
+    return (8 if res else 6 if gate else 4) * R * H + 4 * R + sw * H
 
 
-def bwd_bytes(R, H, sw, dres):
-    return (8 if dres else 6) * R * H + 4 * R + sw * H + 4 * H
+def bwd_bytes(R, H, sw, dres, gate=False):
+    return (8 if dres else 10 if gate else 6) * R * H + 4 * R + sw * H + 4 * H
 
 
 def log(msg):
@@ -79,6 +81,8 @@ class Workload:
 
         self.name = name
         T, heads, H, st, sh, wdt, res = WORKLOADS[name]
+        self.gate = res == "gate"
+        res = res is True
         self.T, self.heads, self.H, self.st, self.sh, self.wdt, self.res = T, heads, H, st, sh, wdt, res
         self.R = T * heads
         self.sw = 4 if wdt == "f32" else 2
@@ -105,6 +109,9 @@ class Workload:
         # the incoming gradient of h for the residual backward's second form
         # (dres ~ N(0,1)); the step itself takes dres = NULL
         self.dres = self.view(place(synth.rows(seed, "dres", 0, self.R, H))) if res else None
+        self.g_h = synth.rows(seed, "g", 0, self.R, H) if self.gate else None
+        self.g = self.view(place(self.g_h)) if self.gate else None
+        self.dg = self.view(place(self.x_h)) if self.gate else None
         self.w = (torch.from_numpy(self.w_h).to(dev) if wdt == "f32" else
                   torch.from_numpy(self.w_h.view(np.int16)).view(torch.bfloat16).to(dev))
         self.y = self.view(place(self.x_h))
@@ -113,16 +120,23 @@ class Workload:
         self.rstd = torch.empty(self.R, dtype=torch.float32, device=dev)
         self.dw = torch.empty(H, dtype=torch.float32, device=dev)
         self.ws = rn.rmsnorm_bwd_workspace(T, heads, H, dev)
-        self.fwd_bytes = fwd_bytes(self.R, H, self.sw, res)
-        self.bwd_bytes = bwd_bytes(self.R, H, self.sw, False)
+        self.fwd_bytes = fwd_bytes(self.R, H, self.sw, res, self.gate)
+        self.bwd_bytes = bwd_bytes(self.R, H, self.sw, False, self.gate)
         self.step_bytes = 2 * self.fwd_bytes + self.bwd_bytes
         self.rn = rn
 
     def fwd(self):
+        if self.gate:
+            self.rn.rmsnorm_gated_fwd(self.x, self.g, self.w, EPS, y=self.y, rstd=self.rstd)
+            return
         self.rn.rmsnorm_fwd(self.x, self.w, EPS, residual=self.r, y=self.y, residual_out=self.h,
                             rstd=self.rstd)
 
     def bwd(self, det=True, dres=None):
+        if self.gate:
+            self.rn.rmsnorm_gated_bwd(self.dy, self.x, self.g, self.rstd, self.w, deterministic=det, dx=self.dx,
+                                      dg=self.dg, dw=self.dw, workspace=self.ws)
+            return
         u = self.h if self.res else self.x
         self.rn.rmsnorm_bwd(self.dy, u, self.rstd, self.w, residual=dres, deterministic=det, dx=self.dx,
                             dw=self.dw, workspace=self.ws)
@@ -215,7 +229,7 @@ def cpu_baseline(wl: Workload, min_seconds=10.0, max_seconds=30.0):
         if time.time() - t_start > max_seconds:
             break
     sec = statistics.median(steps)
-    sample_bytes = 2 * fwd_bytes(rows, wl.H, wl.sw, wl.res) + bwd_bytes(rows, wl.H, wl.sw, False)
+    sample_bytes = 2 * fwd_bytes(rows, wl.H, wl.sw, wl.res, wl.gate) + bwd_bytes(rows, wl.H, wl.sw, False, wl.gate)
     return {"value": sample_bytes / sec / 1e9, "unit": "GB/s", "cores": nthreads, "kind": "oracle",
             "sample": f"2xfwd+bwd over rows 0..{rows - 1} of {wl.R} (H={wl.H}), median of {len(steps)} "
                       f"repeats, {sec:.2f} s per step, {time.time() - t_start:.1f} s in all",
@@ -439,6 +453,16 @@ def _step_oracle(wl, rows):
     x = _rows_view(wl.x_h, rows)
     r = _rows_view(wl.r_h, rows) if wl.res else None
     dy = _rows_view(wl.dy_h, rows)
+    if wl.gate:
+        g = _rows_view(wl.g_h, rows)
+        t0 = time.perf_counter()
+        oracle.gated_fwd_bf16(x, g, wl.w_h, EPS)
+        t1 = time.perf_counter()
+        _, rstd = oracle.gated_fwd_bf16(x, g, wl.w_h, EPS)
+        t2 = time.perf_counter()
+        oracle.gated_bwd_bf16(x, g, dy, wl.w_h, rstd.astype(np.float32))
+        t3 = time.perf_counter()
+        return t1 - t0, t2 - t1, t3 - t2
     t0 = time.perf_counter()
     oracle.fwd_bf16(x, wl.w_h, EPS, r)
     t1 = time.perf_counter()
@@ -545,7 +569,8 @@ def main():
         "dtype": "bf16 storage; fp32/fp64 accumulation",
         "data": "synthetic (seeded N(0,1) x and dy, w = 1 + 0.1 N(0,1))",
         "config": {"workload": wl.name, "T": wl.T, "heads": wl.heads, "H": wl.H, "w_dtype": wl.wdt,
-                   "residual": wl.res, "step": "fwd + fwd (recompute) + bwd (deterministic)",
+                   "residual": wl.res, "silu_gate": wl.gate,
+                   "step": "fwd + fwd (recompute) + bwd (deterministic)",
                    "step_bytes": wl.step_bytes, "pct_of_peak": round(100 * value / PEAK_GBS, 2)},
     }
 

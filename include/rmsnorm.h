@@ -136,6 +136,31 @@ int rmsnorm_bwd(const void* dy, const void* x, const float* rstd, const void* w,
                 int deterministic, void* stream);
 
 /*
+ * SiLU-gated forward and backward.  The pages name a SiLU-gated training
+ * RMSNorm beside this one, in deterministic and non-deterministic forms
+ * (p1 #8208 PR description), without its formula.  Reading taken: the gate
+ * scales the normalised, weighted row and does not enter the norm,
+ *   y = bf16(u * rstd * w * silu(g)),  silu(g) = g / (1 + exp(-g)),
+ * with the gradients of L = sum dy * y:
+ *   dg = bf16(dy * (xhat * w) * silu'(g)),
+ *   dx, dw = the plain backward's at the gated gradient e = dy * silu(g).
+ * No residual.  g and dg are [T,heads,H] BF16 with the activations' strides;
+ * dg may be g and dx may be dy.  silu is evaluated in FP32 (sigmoid within
+ * ~3 units in the last place), so dx, dg and dw carry its relative error
+ * besides their own rounding; all other arithmetic is as in the plain
+ * calls.  The workspace is the plain backward's (rmsnorm_bwd_workspace_size)
+ * and the same rules apply.
+ */
+int rmsnorm_gated_fwd(const void* x, const void* gate, const void* w, int w_dtype, void* y, float* rstd,
+                      int64_t T, int64_t heads, int64_t H, int64_t stride_t, int64_t stride_h,
+                      double eps, int deterministic, void* stream);
+
+int rmsnorm_gated_bwd(const void* dy, const void* x, const void* gate, const float* rstd, const void* w,
+                      int w_dtype, void* dx, void* dgate, float* dw, void* workspace, size_t workspace_bytes,
+                      int64_t T, int64_t heads, int64_t H, int64_t stride_t, int64_t stride_h,
+                      int deterministic, void* stream);
+
+/*
  * Route inspection and override, for the route-table measurement and for
  * tests that cover both sides of a route edge (p3 #8293 commit message: its
  * pairs test exercises each edge from both sides).  A route names how the

@@ -38,6 +38,8 @@ EXPORTS = (
     "rmsnorm_bwd_route",
     "rmsnorm_bwd_workspace_size_for_route",
     "rmsnorm_bwd_routed",
+    "rmsnorm_gated_fwd",
+    "rmsnorm_gated_bwd",
     "rmsnorm_status_string",
 )
 
@@ -82,6 +84,11 @@ def lib() -> ctypes.CDLL:
     L.rmsnorm_bwd_routed.argtypes = [vp, vp, vp, vp, i32, vp, vp, vp, vp, ctypes.c_size_t,
                                      i64, i64, i64, i64, i64, i32, RmsnRoute, vp]
     L.rmsnorm_bwd_routed.restype = i32
+    L.rmsnorm_gated_fwd.argtypes = [vp, vp, vp, i32, vp, vp, i64, i64, i64, i64, i64, ctypes.c_double, i32, vp]
+    L.rmsnorm_gated_fwd.restype = i32
+    L.rmsnorm_gated_bwd.argtypes = [vp, vp, vp, vp, vp, i32, vp, vp, vp, vp, ctypes.c_size_t,
+                                    i64, i64, i64, i64, i64, i32, vp]
+    L.rmsnorm_gated_bwd.restype = i32
     L.rmsnorm_status_string.argtypes = [i32]
     L.rmsnorm_status_string.restype = ctypes.c_char_p
     _lib = L
@@ -251,3 +258,37 @@ def rmsnorm_bwd_routed(dy, x, rstd, w, route, residual=None, deterministic: bool
                                    _stream(x.device, stream))
     _check("rmsnorm_bwd_routed", st_)
     return dx, dw
+
+
+# ---------------------------------------------------------- SiLU gate ----
+
+def rmsnorm_gated_fwd(x, g, w, eps: float = 1e-6, deterministic: bool = True, *, y=None, rstd=None,
+                      stream=None):
+    """y = bf16(RMSNorm(x) * w * silu(g)) and rstd.  Returns (y, rstd)."""
+    torch = _torch()
+    T, heads, H, st, sh = geometry(x)
+    _same_geometry(x, g, "g")
+    y = _like(x) if y is None else y
+    _same_geometry(x, y, "y")
+    if rstd is None:
+        rstd = torch.empty(T * heads, dtype=torch.float32, device=x.device)
+    _check("rmsnorm_gated_fwd", lib().rmsnorm_gated_fwd(
+        _ptr(x), _ptr(g), _ptr(w), _w_dtype(w), _ptr(y), _ptr(rstd), T, heads, H, st, sh, float(eps),
+        int(bool(deterministic)), _stream(x.device, stream)))
+    return y, rstd
+
+
+def rmsnorm_gated_bwd(dy, x, g, rstd, w, deterministic: bool = True, *, dx=None, dg=None, dw=None,
+                      workspace=None, stream=None):
+    """dx, dg (BF16) and dw (FP32) of the gated forward.  Returns (dx, dg, dw)."""
+    (T, heads, H, st, sh), dx, dw = _bwd_args(dy, x, rstd, w, None, dx, dw)
+    _same_geometry(x, g, "g")
+    dg = _like(x) if dg is None else dg
+    _same_geometry(x, dg, "dg")
+    if workspace is None:
+        workspace = rmsnorm_bwd_workspace(T, heads, H, x.device, deterministic)
+    _check("rmsnorm_gated_bwd", lib().rmsnorm_gated_bwd(
+        _ptr(dy), _ptr(x), _ptr(g), _ptr(rstd), _ptr(w), _w_dtype(w), _ptr(dx), _ptr(dg), _ptr(dw),
+        _ptr(workspace), workspace.numel() * workspace.element_size(), T, heads, H, st, sh,
+        int(bool(deterministic)), _stream(x.device, stream)))
+    return dx, dg, dw

@@ -16,7 +16,7 @@ from __future__ import annotations
 
 import torch
 
-from . import geometry, rmsnorm_bwd, rmsnorm_fwd
+from . import geometry, rmsnorm_bwd, rmsnorm_fwd, rmsnorm_gated_bwd, rmsnorm_gated_fwd
 
 
 def _like_layout(t, ref):
@@ -101,3 +101,35 @@ class RMSNorm(torch.nn.Module):
 
     def forward(self, x, residual=None):
         return rmsnorm(x, self.weight, self.eps, residual, self.deterministic, self.recompute)
+
+
+class GatedRMSNormFunction(torch.autograd.Function):
+    """y = RMSNorm(x) * w * silu(g): the SiLU-gated variant (gradients for
+    x, w and g)."""
+
+    @staticmethod
+    def forward(ctx, x, g, w, eps, deterministic, recompute):
+        ctx.shape = x.shape
+        x, g = _rows(x), _rows(g)
+        ctx.set_materialize_grads(False)
+        y, rstd = rmsnorm_gated_fwd(x, g, w, eps, deterministic=deterministic)
+        ctx.eps, ctx.deterministic, ctx.recompute = eps, deterministic, recompute
+        ctx.save_for_backward(x, g, w, None if recompute else rstd)
+        return y.view(ctx.shape)
+
+    @staticmethod
+    def backward(ctx, dy):
+        x, g, w, rstd = ctx.saved_tensors
+        if dy is None:
+            return None, None, None, None, None, None
+        if ctx.recompute:
+            _, rstd = rmsnorm_gated_fwd(x, g, w, ctx.eps, deterministic=ctx.deterministic)
+        dy = _like_layout(_rows(dy), x)
+        dx, dg, dw = rmsnorm_gated_bwd(dy, x, g, rstd, w, deterministic=ctx.deterministic)
+        grad_w = dw if w.dtype == torch.float32 else dw.to(w.dtype)
+        return dx.view(ctx.shape), dg.view(ctx.shape), grad_w, None, None, None
+
+
+def rmsnorm_gated(x, g, w, eps: float = 1e-6, deterministic: bool = True, recompute: bool = False):
+    """Functional form of :class:`GatedRMSNormFunction`."""
+    return GatedRMSNormFunction.apply(x, g, w, eps, deterministic, recompute)

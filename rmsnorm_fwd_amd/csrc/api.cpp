@@ -74,7 +74,8 @@ int check_route(const Shape& s, const rmsn_route& r, int deterministic)
 
 int bwd_impl(const void* dy, const void* x, const float* rstd, const void* w, int w_dtype,
              const void* dres, void* dx, float* dw, void* workspace, size_t workspace_bytes,
-             const Shape& s, const rmsn_route& route, hipStream_t stream)
+             const Shape& s, const rmsn_route& route, hipStream_t stream,
+             const void* gate = nullptr, void* dgate = nullptr)
 {
     const BwdRoute r{route.form, route.chunks};
     if (s.R == 0) return status_of(launch_fill_zero(dw, s.H * 4, stream));
@@ -86,6 +87,8 @@ int bwd_impl(const void* dy, const void* x, const float* rstd, const void* w, in
     p.rstd = rstd;
     p.w = w;
     p.dres = static_cast<const uint16_t*>(dres);
+    p.g = static_cast<const uint16_t*>(gate);
+    p.dg = static_cast<uint16_t*>(dgate);
     p.dx = static_cast<uint16_t*>(dx);
     p.dw = dw;
     char* ws = static_cast<char*>(workspace);
@@ -120,16 +123,12 @@ int check_bwd_args(const void* dy, const void* x, const float* rstd, const void*
     return RMSN_OK;
 }
 
-}  // namespace
-
-extern "C" {
-
-int rmsnorm_fwd(const void* x, const void* residual, const void* w, int w_dtype,
-                void* y, void* residual_out, float* rstd,
-                int64_t T, int64_t heads, int64_t H, int64_t stride_t, int64_t stride_h,
-                double eps, int deterministic, void* stream)
+// Forward with an optional residual (r, h) or an optional SiLU gate.
+int fwd_impl(const void* x, const void* residual, const void* gate, const void* w, int w_dtype,
+             void* y, void* residual_out, float* rstd,
+             int64_t T, int64_t heads, int64_t H, int64_t stride_t, int64_t stride_h,
+             double eps, void* stream)
 {
-    (void)deterministic;  // the forward is one program for both modes
     Shape s;
     int st = check_shape(T, heads, H, stride_t, stride_h, &s);
     if (st != RMSN_OK) return st;
@@ -139,7 +138,7 @@ int rmsnorm_fwd(const void* x, const void* residual, const void* w, int w_dtype,
     if (!x || !w || !y || !rstd) return RMSN_ERR_INVALID_ARG;
     if ((residual != nullptr) != (residual_out != nullptr)) return RMSN_ERR_INVALID_ARG;
     if (!aligned(x, 16) || !aligned(w, 16) || !aligned(y, 16) || !aligned(rstd, 4) ||
-        (residual && (!aligned(residual, 16) || !aligned(residual_out, 16))))
+        (residual && (!aligned(residual, 16) || !aligned(residual_out, 16))) || (gate && !aligned(gate, 16)))
         return RMSN_ERR_MISALIGNED;
 
     const int layout = pick_layout(kFwdLayouts, kNumFwdLayouts, s.H);
@@ -155,6 +154,7 @@ int rmsnorm_fwd(const void* x, const void* residual, const void* w, int w_dtype,
     p.w = w;
     p.y = static_cast<uint16_t*>(y);
     p.h = static_cast<uint16_t*>(residual_out);
+    p.g = static_cast<const uint16_t*>(gate);
     p.rstd = rstd;
     p.rows = make_row_map(s.heads, s.st, s.sh);
     p.R = (int)s.R;
@@ -162,6 +162,33 @@ int rmsnorm_fwd(const void* x, const void* residual, const void* w, int w_dtype,
     p.eps = eps;
     p.inv_h = 1.0 / (double)s.H;
     return status_of(launch_fwd(layout, w_dtype == RMSN_W_F32, p, grid, static_cast<hipStream_t>(stream)));
+}
+
+}  // namespace
+
+extern "C" {
+
+int rmsnorm_fwd(const void* x, const void* residual, const void* w, int w_dtype,
+                void* y, void* residual_out, float* rstd,
+                int64_t T, int64_t heads, int64_t H, int64_t stride_t, int64_t stride_h,
+                double eps, int deterministic, void* stream)
+{
+    (void)deterministic;  // the forward is one program for both modes
+    return fwd_impl(x, residual, nullptr, w, w_dtype, y, residual_out, rstd, T, heads, H, stride_t,
+                    stride_h, eps, stream);
+}
+
+int rmsnorm_gated_fwd(const void* x, const void* gate, const void* w, int w_dtype, void* y, float* rstd,
+                      int64_t T, int64_t heads, int64_t H, int64_t stride_t, int64_t stride_h,
+                      double eps, int deterministic, void* stream)
+{
+    (void)deterministic;
+    Shape s;
+    const int st = check_shape(T, heads, H, stride_t, stride_h, &s);
+    if (st != RMSN_OK) return st;
+    if (s.R > 0 && !gate) return RMSN_ERR_INVALID_ARG;
+    return fwd_impl(x, nullptr, gate, w, w_dtype, y, nullptr, rstd, T, heads, H, stride_t, stride_h, eps,
+                    stream);
 }
 
 size_t rmsnorm_bwd_workspace_size(int64_t T, int64_t heads, int64_t H, int deterministic)
@@ -244,6 +271,25 @@ int rmsnorm_bwd(const void* dy, const void* x, const float* rstd, const void* w,
     if (s.R > 0 && workspace_bytes < ws_bytes_for(s.R, s.H, r)) return RMSN_ERR_WORKSPACE;
     return bwd_impl(dy, x, rstd, w, w_dtype, residual, dx, dw, workspace, workspace_bytes, s, route,
                     static_cast<hipStream_t>(stream));
+}
+
+int rmsnorm_gated_bwd(const void* dy, const void* x, const void* gate, const float* rstd, const void* w,
+                      int w_dtype, void* dx, void* dgate, float* dw, void* workspace, size_t workspace_bytes,
+                      int64_t T, int64_t heads, int64_t H, int64_t stride_t, int64_t stride_h,
+                      int deterministic, void* stream)
+{
+    Shape s;
+    int st = check_shape(T, heads, H, stride_t, stride_h, &s);
+    if (st != RMSN_OK) return st;
+    st = check_bwd_args(dy, x, rstd, w, w_dtype, nullptr, dx, dw, workspace, s);
+    if (st != RMSN_OK) return st;
+    if (s.R > 0 && (!gate || !dgate)) return RMSN_ERR_INVALID_ARG;
+    if (s.R > 0 && (!aligned(gate, 16) || !aligned(dgate, 16))) return RMSN_ERR_MISALIGNED;
+    const BwdRoute r = default_bwd_route(s.R, s.H, w_dtype == RMSN_W_F32, false, deterministic != 0);
+    const rmsn_route route{r.form, r.chunks};
+    if (s.R > 0 && workspace_bytes < ws_bytes_for(s.R, s.H, r)) return RMSN_ERR_WORKSPACE;
+    return bwd_impl(dy, x, rstd, w, w_dtype, nullptr, dx, dw, workspace, workspace_bytes, s, route,
+                    static_cast<hipStream_t>(stream), gate, dgate);
 }
 
 const char* rmsnorm_status_string(int status)

@@ -61,19 +61,20 @@ __device__ __forceinline__ double chunk_group_sum(const double* part, int chunks
 }
 
 // One iteration's rows of a row group: addresses, rstd and the x / dy (and
-// dres) vectors, all loaded before any of them is used.
-template <int U, int V, bool DRES>
+// dres, or the gate g) vectors, all loaded before any of them is used.
+// DRES and GATE never meet.
+template <int U, int V, bool DRES, bool GATE>
 struct BwdTile {
     bool ok[U];
     int64_t off[U];
     double rho[U];
     uint4 xv[U][V], dv[U][V];
-    uint4 rv[DRES ? U : 1][DRES ? V : 1];
+    uint4 rv[(DRES || GATE) ? U : 1][(DRES || GATE) ? V : 1];
 };
 
-template <int U, int V, int SLOTS, bool DRES>
-__device__ __forceinline__ void bwd_load(BwdTile<U, V, DRES>& t, const BwdParams& p, const LaneVectors<V>& lv,
-                                         int base, int slot, int row1)
+template <int U, int V, int SLOTS, bool DRES, bool GATE>
+__device__ __forceinline__ void bwd_load(BwdTile<U, V, DRES, GATE>& t, const BwdParams& p,
+                                         const LaneVectors<V>& lv, int base, int slot, int row1)
 {
 #pragma unroll
     for (int u = 0; u < U; ++u) {
@@ -90,10 +91,11 @@ __device__ __forceinline__ void bwd_load(BwdTile<U, V, DRES>& t, const BwdParams
             t.xv[u][v] = ld16_stream(p.x + t.off[u] + lv.col[v]);
             t.dv[u][v] = ld16_stream(p.dy + t.off[u] + lv.col[v]);
             if constexpr (DRES) t.rv[u][v] = ld16_stream(p.dres + t.off[u] + lv.col[v]);
+            if constexpr (GATE) t.rv[u][v] = ld16_stream(p.g + t.off[u] + lv.col[v]);
         }
 }
 
-template <int LPR, int V, int U, bool WF32, bool DRES>
+template <int LPR, int V, int U, bool WF32, bool DRES, bool GATE>
 __global__ void __launch_bounds__(block_of(LPR)) bwd_kernel(BwdParams p)
 {
     constexpr int BLOCK = block_of(LPR);
@@ -140,10 +142,10 @@ __global__ void __launch_bounds__(block_of(LPR)) bwd_kernel(BwdParams p)
 #pragma unroll
         for (int e = 0; e < 8; ++e) acc[v][e] = 0.0;
 
-    BwdTile<U, V, DRES> cur;
+    BwdTile<U, V, DRES, GATE> cur;
     int it = 0;
     for (int base = first; base < row1; base += step, ++it) {
-        bwd_load<U, V, SLOTS, DRES>(cur, p, lv, base, slot, row1);
+        bwd_load<U, V, SLOTS, DRES, GATE>(cur, p, lv, base, slot, row1);
         const bool* ok = cur.ok;
         const int64_t* off = cur.off;
         const double* rho = cur.rho;
@@ -158,9 +160,18 @@ __global__ void __launch_bounds__(block_of(LPR)) bwd_kernel(BwdParams p)
                 float xf[8], df[8];
                 unpack8(xv[u][v], xf);
                 unpack8(dv[u][v], df);
+                float sg[8];  // silu(g) with a gate, else unused
+                if constexpr (GATE) {
+                    float gf[8];
+                    unpack8(cur.rv[u][v], gf);
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) sg[e] = gf[e] * sigmoid_f32(gf[e]);
+                }
 #pragma unroll
                 for (int e = 0; e < 8; ++e) {
-                    const double pd = (double)(xf[e] * df[e]);
+                    // x * dy is exact in FP32; times silu(g) (24 bits) still exact in FP64
+                    double pd = (double)(xf[e] * df[e]);
+                    if constexpr (GATE) pd *= (double)sg[e];
                     acc[v][e] = __builtin_fma(pd, rho[u], acc[v][e]);
                     S[u] = __builtin_fma(pd, w64[v][e], S[u]);
                 }
@@ -175,14 +186,26 @@ __global__ void __launch_bounds__(block_of(LPR)) bwd_kernel(BwdParams p)
                 float xf[8], df[8], rf[8];
                 unpack8(xv[u][v], xf);
                 unpack8(dv[u][v], df);
-                if constexpr (DRES) unpack8(cur.rv[u][v], rf);
+                if constexpr (DRES || GATE) unpack8(cur.rv[u][v], rf);
                 double d[8];
+                float q[8];
 #pragma unroll
                 for (int e = 0; e < 8; ++e) {
-                    const double gw = w64[v][e] * (double)df[e];  // exact
+                    double ge = (double)df[e];  // gradient reaching the normalised row
+                    if constexpr (GATE) {
+                        // dy * silu(g) (exact in FP64), and dg = dy * (xhat * w) * silu'(g)
+                        // in FP32 (its rounding stays below silu''s own error)
+                        const float sgm = sigmoid_f32(rf[e]);
+                        const float dsilu = sgm * __builtin_fmaf(rf[e], 1.0f - sgm, 1.0f);
+                        ge *= (double)(rf[e] * sgm);
+                        q[e] = (df[e] * ((xf[e] * (float)rho[u]) * (float)w64[v][e])) * dsilu;
+                    }
+                    const double gw = w64[v][e] * ge;  // exact without a gate
                     d[e] = __builtin_fma(gw, rho[u], -((double)xf[e] * L));
                     if constexpr (DRES) d[e] += (double)rf[e];
                 }
+                if constexpr (GATE)
+                    if (ok[u] && lv.ok[v]) st16_stream(p.dg + off[u] + lv.col[v], pack8(q));
                 uint4 o;
                 o.x = pack_bf16x2_from_f64(d[0], d[1]);
                 o.y = pack_bf16x2_from_f64(d[2], d[3]);
@@ -297,42 +320,61 @@ __global__ void fill_zero_kernel(uint32_t* p, int64_t words)
 
 // ----------------------------------------------------------- launchers ----
 
-template <int LPR, int V, int U, bool WF32, bool DRES>
+template <int LPR, int V, int U, bool WF32, bool DRES, bool GATE>
 static hipError_t bwd_t(const BwdParams& p, hipStream_t s)
 {
     constexpr int SLOTS = slots_of(LPR);
     constexpr int ROWS = LPR < 64 ? block_of(LPR) / 64 : SLOTS;
     const size_t lds = SLOTS > 1 ? (size_t)ROWS * p.H * sizeof(double) : 0;
     if (lds > (size_t)kMaxSlotLds) return hipErrorInvalidConfiguration;
-    hipLaunchKernelGGL((bwd_kernel<LPR, V, U, WF32, DRES>), dim3(p.chunks), dim3(block_of(LPR)), lds, s, p);
+    hipLaunchKernelGGL((bwd_kernel<LPR, V, U, WF32, DRES, GATE>), dim3(p.chunks), dim3(block_of(LPR)), lds, s, p);
     return hipGetLastError();
 }
+
+template <int LPR, int V, int U, bool DRES, bool GATE>
+static hipError_t bwd_w(bool w_f32, const BwdParams& p, hipStream_t s)
+{
+    return w_f32 ? bwd_t<LPR, V, U, true, DRES, GATE>(p, s) : bwd_t<LPR, V, U, false, DRES, GATE>(p, s);
+}
+
+// Gated rows hold one more input per element and evaluate silu twice: with
+// more than one row per row group they outgrow the 256 registers a lane has
+// at two wavefronts per SIMD, so they take one.
+template <int LPR, int V, int U>
+constexpr int gated_u() { return LPR <= 256 ? 1 : U; }
 
 template <int LPR, int V, int U>
 static hipError_t bwd_dispatch(bool w_f32, const BwdParams& p, hipStream_t s)
 {
-    if (p.dres) return w_f32 ? bwd_t<LPR, V, U, true, true>(p, s) : bwd_t<LPR, V, U, false, true>(p, s);
-    return w_f32 ? bwd_t<LPR, V, U, true, false>(p, s) : bwd_t<LPR, V, U, false, false>(p, s);
+    if (p.dres) return bwd_w<LPR, V, U, true, false>(w_f32, p, s);
+    if (p.g) return bwd_w<LPR, V, gated_u<LPR, V, U>(), false, true>(w_f32, p, s);
+    return bwd_w<LPR, V, U, false, false>(w_f32, p, s);
 }
 
 // Single-workgroup path: the smallest U in {1, 2, 4} (up to direct_max_u)
-// whose one iteration covers every row.
+// whose one iteration covers every row; gated rows keep gated_u.
+template <int LPR, int V, int U, bool DRES, bool GATE>
+static hipError_t bwd_direct_t(bool w_f32, const BwdParams& p, hipStream_t s)
+{
+    constexpr int UM = direct_max_u(LPR, V, U);
+    constexpr int UMAX = GATE ? gated_u<LPR, V, U>() : UM;
+    constexpr int SL = slots_of(LPR);
+    if constexpr (UMAX >= 2) {
+        if (p.R <= SL) return bwd_w<LPR, V, 1, DRES, GATE>(w_f32, p, s);
+        if constexpr (UMAX >= 4)
+            if (p.R > 2 * SL) return bwd_w<LPR, V, 4, DRES, GATE>(w_f32, p, s);
+        return bwd_w<LPR, V, 2, DRES, GATE>(w_f32, p, s);
+    } else {
+        return bwd_w<LPR, V, UMAX, DRES, GATE>(w_f32, p, s);
+    }
+}
+
 template <int LPR, int V, int U>
 static hipError_t bwd_direct(bool w_f32, const BwdParams& p, hipStream_t s)
 {
-    constexpr int UMAX = direct_max_u(LPR, V, U);
-    constexpr int SL = slots_of(LPR);
-    if constexpr (UMAX >= 2 && U < UMAX) {
-        if (p.R <= SL) return bwd_dispatch<LPR, V, 1>(w_f32, p, s);
-        if constexpr (UMAX >= 4)
-            if (p.R > 2 * SL) return bwd_dispatch<LPR, V, 4>(w_f32, p, s);
-        return bwd_dispatch<LPR, V, 2>(w_f32, p, s);
-    } else if constexpr (UMAX >= 2) {
-        if (p.R <= SL) return bwd_dispatch<LPR, V, 1>(w_f32, p, s);
-        return bwd_dispatch<LPR, V, UMAX>(w_f32, p, s);
-    } else {
-        return bwd_dispatch<LPR, V, U>(w_f32, p, s);
-    }
+    if (p.dres) return bwd_direct_t<LPR, V, U, true, false>(w_f32, p, s);
+    if (p.g) return bwd_direct_t<LPR, V, U, false, true>(w_f32, p, s);
+    return bwd_direct_t<LPR, V, U, false, false>(w_f32, p, s);
 }
 
 hipError_t launch_bwd(int layout, bool w_f32, const BwdParams& p, hipStream_t s)

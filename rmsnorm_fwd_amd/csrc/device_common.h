@@ -35,6 +35,27 @@ __device__ __forceinline__ uint32_t pack_bf16x2_from_f64(double lo, double hi)
     return pack_bf16x2(a, b);
 }
 
+// SiLU gate in FP32: sigmoid(g) = 1 / (1 + exp(-g)), silu = g * sigmoid,
+// silu' = sigmoid * (1 + g * (1 - sigmoid)).  exp(-g) = 2^t with
+// t = -g * log2(e) carried as a rounded product p plus its error (an FMA
+// gives the product's rounding error exactly; log2(e)'s own tail is added),
+// so the hardware 2^p (v_exp_f32, 1 unit) is corrected by 2^lo ~ 1 + lo ln 2.
+// p is clamped to [-126, 126]: beyond it sigmoid is 1, or below 2^-126 and
+// only adds below 1e-36 to silu.  The reciprocal is v_rcp_f32 (1 unit), so
+// sigmoid is within ~4 units in the last place over the whole range.
+__device__ __forceinline__ float sigmoid_f32(float g)
+{
+    constexpr float kL2eHi = 1.44269502162933349609375f;   // log2(e) rounded to float
+    constexpr float kL2eLo = 1.925963033500011e-08f;        // log2(e) - kL2eHi
+    constexpr float kLn2 = 0.693147180559945309f;
+    const float p = -g * kL2eHi;
+    const float lo = __builtin_fmaf(-g, kL2eLo, __builtin_fmaf(-g, kL2eHi, -p));
+    const float pc = __builtin_amdgcn_fmed3f(p, -126.0f, 126.0f);
+    const float e0 = __builtin_amdgcn_exp2f(pc);
+    const float e = pc == p ? __builtin_fmaf(e0, lo * kLn2, e0) : e0;
+    return __builtin_amdgcn_rcpf(1.0f + e);
+}
+
 __device__ __forceinline__ void unpack8(const uint4& v, float f[8])
 {
     f[0] = bf_lo(v.x); f[1] = bf_hi(v.x);

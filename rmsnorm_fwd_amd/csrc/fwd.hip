@@ -18,19 +18,20 @@
 
 namespace rmsn {
 
-// One iteration's rows of a row group: validity, addresses, x (and r) vectors.
-template <int U, int V, bool RES>
+// One iteration's rows of a row group: validity, addresses, x (and r, or
+// the gate g) vectors.  RES and GATE never meet.
+template <int U, int V, bool RES, bool GATE>
 struct FwdTile {
     int row[U];
     bool ok[U];
     int64_t off[U];
     uint4 xv[U][V];
-    uint4 rv[RES ? U : 1][RES ? V : 1];
+    uint4 rv[(RES || GATE) ? U : 1][(RES || GATE) ? V : 1];
 };
 
-template <int U, int V, int SLOTS, bool RES>
-__device__ __forceinline__ void fwd_load(FwdTile<U, V, RES>& t, const FwdParams& p, const LaneVectors<V>& lv,
-                                         int base, int slot)
+template <int U, int V, int SLOTS, bool RES, bool GATE>
+__device__ __forceinline__ void fwd_load(FwdTile<U, V, RES, GATE>& t, const FwdParams& p,
+                                         const LaneVectors<V>& lv, int base, int slot)
 {
 #pragma unroll
     for (int u = 0; u < U; ++u) {
@@ -44,10 +45,11 @@ __device__ __forceinline__ void fwd_load(FwdTile<U, V, RES>& t, const FwdParams&
         for (int v = 0; v < V; ++v) {
             t.xv[u][v] = ld16_stream(p.x + t.off[u] + lv.col[v]);
             if constexpr (RES) t.rv[u][v] = ld16_stream(p.r + t.off[u] + lv.col[v]);
+            if constexpr (GATE) t.rv[u][v] = ld16_stream(p.g + t.off[u] + lv.col[v]);
         }
 }
 
-template <int LPR, int V, int U, bool WF32, bool RES>
+template <int LPR, int V, int U, bool WF32, bool RES, bool GATE>
 __global__ void __launch_bounds__(block_of(LPR)) fwd_kernel(FwdParams p)
 {
     constexpr int BLOCK = block_of(LPR);
@@ -77,10 +79,10 @@ __global__ void __launch_bounds__(block_of(LPR)) fwd_kernel(FwdParams p)
     }
 
     const int stride = gridDim.x * RPI;
-    FwdTile<U, V, RES> cur;
+    FwdTile<U, V, RES, GATE> cur;
     int it = 0;
     for (int base = blockIdx.x * RPI; base < p.R; base += stride, ++it) {
-        fwd_load<U, V, SLOTS, RES>(cur, p, lv, base, slot);
+        fwd_load<U, V, SLOTS, RES, GATE>(cur, p, lv, base, slot);
         const int* row = cur.row;
         const bool* ok = cur.ok;
         const int64_t* off = cur.off;
@@ -133,24 +135,38 @@ __global__ void __launch_bounds__(block_of(LPR)) fwd_kernel(FwdParams p)
                 }
 #pragma unroll
                 for (int e = 0; e < 8; ++e) f[e] = (f[e] * rs) * wv[e];
+                if constexpr (GATE) {
+                    // y = (u * rstd * w) * silu(g), all in FP32
+                    float gf[8];
+                    unpack8(cur.rv[u][v], gf);
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) f[e] *= gf[e] * sigmoid_f32(gf[e]);
+                }
                 if (ok[u] && lv.ok[v]) st16_stream(p.y + off[u] + lv.col[v], pack8(f));
             }
         }
     }
 }
 
-template <int LPR, int V, int U, bool WF32, bool RES>
+template <int LPR, int V, int U, bool WF32, bool RES, bool GATE>
 static hipError_t fwd_t(const FwdParams& p, int grid, hipStream_t s)
 {
-    hipLaunchKernelGGL((fwd_kernel<LPR, V, U, WF32, RES>), dim3(grid), dim3(block_of(LPR)), 0, s, p);
+    hipLaunchKernelGGL((fwd_kernel<LPR, V, U, WF32, RES, GATE>), dim3(grid), dim3(block_of(LPR)), 0, s, p);
     return hipGetLastError();
+}
+
+template <int LPR, int V, int U, bool RES, bool GATE>
+static hipError_t fwd_w(bool w_f32, const FwdParams& p, int grid, hipStream_t s)
+{
+    return w_f32 ? fwd_t<LPR, V, U, true, RES, GATE>(p, grid, s) : fwd_t<LPR, V, U, false, RES, GATE>(p, grid, s);
 }
 
 template <int LPR, int V, int U>
 static hipError_t fwd_dispatch(bool w_f32, const FwdParams& p, int grid, hipStream_t s)
 {
-    if (p.r) return w_f32 ? fwd_t<LPR, V, U, true, true>(p, grid, s) : fwd_t<LPR, V, U, false, true>(p, grid, s);
-    return w_f32 ? fwd_t<LPR, V, U, true, false>(p, grid, s) : fwd_t<LPR, V, U, false, false>(p, grid, s);
+    if (p.r) return fwd_w<LPR, V, U, true, false>(w_f32, p, grid, s);
+    if (p.g) return fwd_w<LPR, V, U, false, true>(w_f32, p, grid, s);
+    return fwd_w<LPR, V, U, false, false>(w_f32, p, grid, s);
 }
 
 hipError_t launch_fwd(int layout, bool w_f32, const FwdParams& p, int grid, hipStream_t s)

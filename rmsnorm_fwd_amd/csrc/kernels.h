@@ -38,6 +38,7 @@ struct FwdParams {
     const void* w;        // [H] BF16 or FP32
     uint16_t* y;          // [T,heads,H] BF16
     uint16_t* h;          // residual output (when r != nullptr)
+    const uint16_t* g;    // SiLU gate [T,heads,H] or nullptr (never with r)
     float* rstd;          // [R]
     RowMap rows;
     int R, H;
@@ -50,6 +51,8 @@ struct BwdParams {
     const float* rstd;
     const void* w;
     const uint16_t* dres; // or nullptr
+    const uint16_t* g;    // SiLU gate or nullptr (never with dres)
+    uint16_t* dg;         // gate gradient (when g != nullptr)
     uint16_t* dx;
     float* dw;
     double* part;         // [P,H] FP64 chunk partials (pair form)

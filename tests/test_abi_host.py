@@ -183,3 +183,48 @@ def test_row_count_limit_is_below_2_pow_30():
         assert L.rmsnorm_bwd_route(last + 1, heads, 256, 0, 0, 1, ctypes.byref(r)) == rn.RMSN_ERR_INVALID_ARG
         assert rn.rmsnorm_bwd_workspace_size(last, heads, 256) > 0
         assert rn.rmsnorm_bwd_workspace_size(last + 1, heads, 256) == 0
+
+
+def _gfwd(**kw):
+    a = dict(x=GOOD, g=GOOD, w=GOOD, wd=0, y=GOOD, rstd=GOOD, T=4, heads=1, H=64, st=64, sh=64, eps=1e-6)
+    a.update(kw)
+    return rn.lib().rmsnorm_gated_fwd(a["x"], a["g"], a["w"], a["wd"], a["y"], a["rstd"], a["T"], a["heads"],
+                                      a["H"], a["st"], a["sh"], a["eps"], 1, None)
+
+
+def _gbwd(**kw):
+    a = dict(dy=GOOD, x=GOOD, g=GOOD, rstd=GOOD, w=GOOD, wd=0, dx=GOOD, dg=GOOD, dw=GOOD, ws=GOOD,
+             wsb=1 << 30, T=4, heads=1, H=64, st=64, sh=64, det=1)
+    a.update(kw)
+    return rn.lib().rmsnorm_gated_bwd(a["dy"], a["x"], a["g"], a["rstd"], a["w"], a["wd"], a["dx"], a["dg"],
+                                      a["dw"], a["ws"], a["wsb"], a["T"], a["heads"], a["H"], a["st"], a["sh"],
+                                      a["det"], None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(g=None), rn.RMSN_ERR_INVALID_ARG),
+    (dict(g=BAD), rn.RMSN_ERR_MISALIGNED),
+    (dict(H=12, st=12, sh=12), rn.RMSN_ERR_UNSUPPORTED),
+    (dict(eps=-1.0), rn.RMSN_ERR_INVALID_ARG),
+    (dict(st=32), rn.RMSN_ERR_INVALID_ARG),
+    (dict(y=None), rn.RMSN_ERR_INVALID_ARG),
+])
+def test_gated_fwd_rejects_bad_arguments(kw, status):
+    assert _gfwd(**kw) == status
+
+
+def test_gated_fwd_zero_rows_is_a_no_op():
+    assert _gfwd(T=0, x=None, g=None, y=None, rstd=None) == rn.RMSN_OK
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(g=None), rn.RMSN_ERR_INVALID_ARG),
+    (dict(dg=None), rn.RMSN_ERR_INVALID_ARG),
+    (dict(g=BAD), rn.RMSN_ERR_MISALIGNED),
+    (dict(dg=BAD), rn.RMSN_ERR_MISALIGNED),
+    (dict(dw=None), rn.RMSN_ERR_INVALID_ARG),
+    (dict(wsb=16), rn.RMSN_ERR_WORKSPACE),
+    (dict(wd=5), rn.RMSN_ERR_INVALID_ARG),
+])
+def test_gated_bwd_rejects_bad_arguments(kw, status):
+    assert _gbwd(**kw) == status

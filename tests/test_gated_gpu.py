@@ -1,0 +1,142 @@
+"""SiLU-gated variant (y = RMSNorm(x) * w * silu(g)) through the C ABI against
+the oracle.
+
+Tolerances.  The kernels evaluate silu in FP32: sigmoid(g) = 1 / (1 + exp(-g))
+is within ~3 units in the last place of FP32, so silu and silu' carry a
+relative error below EPS_S = 2^-20 (a margin of ~4 over that bound).
+  * y: within 1 BF16 unit (its FP32 error stays far below half a BF16 unit).
+  * rstd: as in the plain forward (the gate does not enter the norm).
+  * dx: within 1 BF16 unit, or within one unit plus the bound that silu's
+    error sets on the FP64 evaluation: EPS_S * rho * (|w e| + |x| rho^2
+    sum_i |x_i w_i e_i| / H), e = dy * silu(g).
+  * dg: within 1 BF16 unit, or one unit plus EPS_S * |dy * xhat * w| *
+    sigmoid(g) * (1 + 2 |g|) (silu' = sigmoid (1 + g (1 - sigmoid)) cancels
+    near g = -1.28).
+  * dw: the plain budget 1e-4 + 1e-4 |dw| plus EPS_S * sum over rows of
+    |e * xhat|.
+dx and dg are bitwise the same in both modes; deterministic dw repeats
+bitwise."""
+import numpy as np
+import pytest
+
+import oracle
+import synth
+from tests.helpers import EPS, Layout, to_dev_bf16, to_host_bits, ulp_dist, weight_dev
+
+pytestmark = pytest.mark.gpu
+
+EPS_S = 2.0 ** -20
+
+
+def _bf16_ulp(v):
+    """Spacing of BF16 numbers at |v| (subnormal floor included)."""
+    a = np.maximum(np.abs(v), 2.0 ** -126)
+    return 2.0 ** (np.floor(np.log2(a)) - 7)
+
+
+def _close(got_bits, ref64, bound):
+    got = oracle.bf16_to_f64(got_bits)
+    ok = ulp_dist(got_bits, oracle.bf16_round(ref64)) <= 1
+    ok |= np.abs(got - ref64) <= _bf16_ulp(ref64) + bound
+    return ok
+
+
+def gen_gate(seed, R, H, kind):
+    g = synth.rows(seed, "g", 0, R, H, "offset" if kind == "open" else "normal")
+    if kind == "mixed":
+        gf = oracle.bf16_to_f64(g).reshape(-1)
+        gf[::7] *= 6.0                         # wide gates, both tails
+        gf[1::11] = 0.0                        # closed gate
+        gf[2::13] = -1.28125                   # near silu's minimum (silu' ~ 0)
+        gf[3::17] = 30.0                       # saturated: silu = g, silu' = 1
+        g = oracle.bf16_round(gf).reshape(R, H)
+    return g
+
+
+def run_gated(L: Layout, wdt="bf16", seed=0, kind="mixed", det_repeats=2):
+    import torch
+    import rmsnorm_fwd_amd as rn
+    x = synth.rows(seed, "x", 0, L.R, L.H)
+    dy = synth.rows(seed, "dy", 0, L.R, L.H)
+    g = gen_gate(seed, L.R, L.H, kind)
+    w = synth.weight(seed, L.H, wdt)
+    xb, dyb, gb = L.place(x), L.place(dy), L.place(g)
+    wd = weight_dev(w)
+    gaps = L.gap_mask() if L.R else np.zeros(0, bool)
+
+    outs = []
+    for det in (True, False):
+        yb = L.empty()
+        rstd = torch.empty(L.R, dtype=torch.float32, device="cuda")
+        rn.rmsnorm_gated_fwd(L.view(xb), L.view(gb), wd, EPS, deterministic=det, y=L.view(yb), rstd=rstd)
+        outs.append((L.rows_of(yb), rstd.cpu().numpy()))
+        if gaps.any():
+            assert np.all(to_host_bits(yb)[gaps] == 0x7FC0), "write outside the view"
+    assert np.array_equal(outs[0][0], outs[1][0]) and np.array_equal(outs[0][1], outs[1][1])
+    y_k, rho = outs[0]
+    ref_y, ref_rstd = oracle.gated_fwd_bf16(x, g, w, EPS)
+    assert ulp_dist(y_k, ref_y).max(initial=0) <= 1, "y off by more than one unit"
+    if L.R:
+        assert (np.abs(rho.astype(np.float64) - ref_rstd) / ref_rstd).max() <= 1e-6
+
+    ref_dx, ref_dg, dx64, dg64, ref_dw = oracle.gated_bwd_bf16(x, g, dy, w, rho, want_f64=True)
+    # tolerance terms from the FP64 inputs
+    xf, gf, df = oracle.bf16_to_f64(x), oracle.bf16_to_f64(g), oracle.bf16_to_f64(dy)
+    wf = oracle.bf16_to_f64(w) if wdt == "bf16" else w.astype(np.float64)
+    r = rho.astype(np.float64)[:, None]
+    sg = 1.0 / (1.0 + np.exp(-gf))
+    e = df * gf * sg
+    xhat = xf * r
+    bx = EPS_S * r * (np.abs(wf * e) + np.abs(xf) * r * r * np.abs(xf * wf * e).sum(1, keepdims=True) / L.H)
+    bg = EPS_S * np.abs(df * xhat * wf) * sg * (1 + 2 * np.abs(gf))
+    bw = 1e-4 + 1e-4 * np.abs(ref_dw) + EPS_S * np.abs(e * xhat).sum(0)
+    ws = rn.rmsnorm_bwd_workspace(L.T, L.heads, L.H, "cuda")
+    first = {}
+    for det in (True, False):
+        for rep in range(det_repeats if det else 1):
+            dxb, dgb = L.empty(), L.empty()
+            dw = torch.empty(L.H, dtype=torch.float32, device="cuda")
+            rn.rmsnorm_gated_bwd(L.view(dyb), L.view(xb), L.view(gb), torch.from_numpy(rho).cuda(), wd,
+                                 deterministic=det, dx=L.view(dxb), dg=L.view(dgb), dw=dw, workspace=ws)
+            torch.cuda.synchronize()
+            dx_k, dg_k, dw_k = L.rows_of(dxb), L.rows_of(dgb), dw.cpu().numpy()
+            if not first:
+                assert _close(dx_k, dx64, bx).all(), "dx outside its tolerance"
+                assert _close(dg_k, dg64, bg).all(), "dg outside its tolerance"
+                assert (np.abs(dw_k.astype(np.float64) - ref_dw) <= bw).all(), "dw outside its tolerance"
+                first = dict(dx=dx_k, dg=dg_k, dw=dw_k)
+                if gaps.any():
+                    for buf in (dxb, dgb):
+                        assert np.all(to_host_bits(buf)[gaps] == 0x7FC0), "write outside the view"
+            else:
+                assert np.array_equal(dx_k, first["dx"]) and np.array_equal(dg_k, first["dg"])
+                if det:
+                    assert np.array_equal(dw_k, first["dw"]), "deterministic dw not reproducible"
+                else:
+                    assert (np.abs(dw_k.astype(np.float64) - ref_dw) <= bw).all()
+    return ulp_dist(first["dx"], ref_dx).max(initial=0), ulp_dist(first["dg"], ref_dg).max(initial=0)
+
+
+@pytest.mark.parametrize("H", [8, 64, 256, 264, 1024, 1536, 2048, 4096, 5120, 6144, 8192])
+@pytest.mark.parametrize("wdt", ["bf16", "f32"])
+def test_gated_widths(H, wdt):
+    T = 37 if H >= 4096 else 301
+    print(H, wdt, run_gated(Layout.plain(T, H), wdt, seed=H))
+
+
+@pytest.mark.parametrize("T", [0, 1, 2, 3, 5, 17, 64, 65, 1000])
+def test_gated_row_counts(T):
+    print(T, run_gated(Layout.plain(T, 4096), "f32", seed=T + 1))
+
+
+@pytest.mark.parametrize("kind", ["normal", "open", "mixed"])
+def test_gated_gate_families(kind):
+    print(kind, run_gated(Layout.plain(2048, 2048), "bf16", seed=7, kind=kind))
+
+
+def test_gated_head_view():
+    print(run_gated(Layout.heads_view(512, 24, 256, 8192, 256), "bf16", seed=3))
+
+
+def test_gated_large():
+    print(run_gated(Layout.plain(16384, 4096), "f32", seed=5, det_repeats=3))
