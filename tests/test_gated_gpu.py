@@ -140,3 +140,28 @@ def test_gated_head_view():
 
 def test_gated_large():
     print(run_gated(Layout.plain(16384, 4096), "f32", seed=5, det_repeats=3))
+
+
+@pytest.mark.parametrize("recompute", [False, True])
+@pytest.mark.parametrize("wdt", ["bf16", "f32"])
+def test_gated_autograd(wdt, recompute):
+    # the autograd form gives the C-ABI results bitwise: x.grad = dx, g.grad = dg,
+    # w.grad = dw (cast to w's dtype), for an upstream gradient dy
+    import torch
+    import rmsnorm_fwd_amd as rn
+    from rmsnorm_fwd_amd.autograd import rmsnorm_gated
+    T, H = 300, 2048
+    x_h, g_h, dy_h = synth.rows(8, "x", 0, T, H), gen_gate(8, T, H, "mixed"), synth.rows(8, "dy", 0, T, H)
+    w_h = synth.weight(8, H, wdt)
+    x = to_dev_bf16(x_h).view(T, H).requires_grad_(True)
+    g = to_dev_bf16(g_h).view(T, H).requires_grad_(True)
+    w = weight_dev(w_h).requires_grad_(True)
+    dy = to_dev_bf16(dy_h).view(T, H)
+    y = rmsnorm_gated(x, g, w, EPS, deterministic=True, recompute=recompute)
+    y.backward(dy)
+    y2, rstd = rn.rmsnorm_gated_fwd(x.detach(), g.detach(), w.detach(), EPS)
+    dx, dg, dw = rn.rmsnorm_gated_bwd(dy, x.detach(), g.detach(), rstd, w.detach())
+    torch.cuda.synchronize()
+    assert torch.equal(y.detach(), y2)
+    assert torch.equal(x.grad, dx) and torch.equal(g.grad, dg)
+    assert torch.equal(w.grad, dw if wdt == "f32" else dw.to(torch.bfloat16))
