@@ -52,6 +52,7 @@ WORKLOADS = {
     "T2048_H5120": (2048, 1, 5120, 5120, 5120, "bf16", False),
     # the SiLU-gated variant (y = RMSNorm(x) * w * silu(g)) at the headline shape
     "T65536_H4096_w32_gate": (65536, 1, 4096, 4096, 4096, "f32", "gate"),
+    "T65536_H6144_gate": (65536, 1, 6144, 6144, 6144, "bf16", "gate"),
 }
 DEFAULT_WORKLOAD = "T65536_H4096_w32"
 

@@ -343,11 +343,24 @@ static hipError_t bwd_w(bool w_f32, const BwdParams& p, hipStream_t s)
 template <int LPR, int V, int U>
 constexpr int gated_u() { return LPR <= 256 ? 1 : U; }
 
+#ifndef RMSN_GATED_WIDE_V3
+#define RMSN_GATED_WIDE_V3 1
+#endif
+// Gated rows of three vectors per lane spill even at one row per row group;
+// they run as rows of three times the lanes and one vector each instead
+// (the gated variant's row order is then its own, fixed per H).
+template <int LPR, int V, int U>
+static hipError_t bwd_gated(bool w_f32, const BwdParams& p, hipStream_t s)
+{
+    if constexpr (RMSN_GATED_WIDE_V3 && V == 3 && LPR <= 256) return bwd_w<3 * LPR, 1, 1, false, true>(w_f32, p, s);
+    else return bwd_w<LPR, V, gated_u<LPR, V, U>(), false, true>(w_f32, p, s);
+}
+
 template <int LPR, int V, int U>
 static hipError_t bwd_dispatch(bool w_f32, const BwdParams& p, hipStream_t s)
 {
     if (p.dres) return bwd_w<LPR, V, U, true, false>(w_f32, p, s);
-    if (p.g) return bwd_w<LPR, V, gated_u<LPR, V, U>(), false, true>(w_f32, p, s);
+    if (p.g) return bwd_gated<LPR, V, U>(w_f32, p, s);
     return bwd_w<LPR, V, U, false, false>(w_f32, p, s);
 }
 
@@ -373,7 +386,7 @@ template <int LPR, int V, int U>
 static hipError_t bwd_direct(bool w_f32, const BwdParams& p, hipStream_t s)
 {
     if (p.dres) return bwd_direct_t<LPR, V, U, true, false>(w_f32, p, s);
-    if (p.g) return bwd_direct_t<LPR, V, U, false, true>(w_f32, p, s);
+    if (p.g) return bwd_gated<LPR, V, U>(w_f32, p, s);
     return bwd_direct_t<LPR, V, U, false, false>(w_f32, p, s);
 }
 
