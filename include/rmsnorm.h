@@ -146,7 +146,7 @@ int rmsnorm_bwd(const void* dy, const void* x, const float* rstd, const void* w,
  *   dx, dw = the plain backward's at the gated gradient e = dy * silu(g).
  * No residual.  g and dg are [T,heads,H] BF16 with the activations' strides;
  * dg may be g and dx may be dy.  silu is evaluated in FP32 (sigmoid within
- * ~3 units in the last place), so dx, dg and dw carry its relative error
+ * ~4 units in the last place), so dx, dg and dw carry its relative error
  * besides their own rounding; all other arithmetic is as in the plain
  * calls.  The workspace is the plain backward's (rmsnorm_bwd_workspace_size)
  * and the same rules apply.
