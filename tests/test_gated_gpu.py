@@ -165,3 +165,50 @@ def test_gated_autograd(wdt, recompute):
     assert torch.equal(y.detach(), y2)
     assert torch.equal(x.grad, dx) and torch.equal(g.grad, dg)
     assert torch.equal(w.grad, dw if wdt == "f32" else dw.to(torch.bfloat16))
+
+
+def test_gated_full_size_headline_shape():
+    # T=65536 x H=4096, FP32 w (the benchmark's gated workload): y, dx, dg on
+    # sampled rows, dw against the oracle's full column sums, dx/dg across
+    # modes and deterministic dw across repeats over the whole tensors
+    import torch
+    import rmsnorm_fwd_amd as rn
+    T, H = 65536, 4096
+    x, dy = synth.rows(0, "x", 0, T, H), synth.rows(0, "dy", 0, T, H)
+    g = gen_gate(0, T, H, "mixed")
+    w = synth.weight(0, H, "f32")
+    X, G, DY = (to_dev_bf16(a).view(T, H) for a in (x, g, dy))
+    W = weight_dev(w)
+    y, rstd = rn.rmsnorm_gated_fwd(X, G, W, EPS)
+    rows = np.unique(np.concatenate([[0, 1, T // 2, T - 1], np.random.default_rng(1).integers(0, T, 384)]))
+    idx = torch.from_numpy(rows).cuda()
+    rho = rstd.cpu().numpy()
+    ref_y, ref_rstd = oracle.gated_fwd_bf16(x[rows], g[rows], w, EPS)
+    assert ulp_dist(to_host_bits(y.index_select(0, idx)), ref_y).max() <= 1
+    assert (np.abs(rho[rows].astype(np.float64) - ref_rstd) / ref_rstd).max() <= 1e-6
+    dx, dg, dw = rn.rmsnorm_gated_bwd(DY, X, G, rstd, W, deterministic=True)
+    _, _, dx64, dg64, _ = oracle.gated_bwd_bf16(x[rows], g[rows], dy[rows], w, rho[rows], want_f64=True)
+    xf, gf, df = oracle.bf16_to_f64(x[rows]), oracle.bf16_to_f64(g[rows]), oracle.bf16_to_f64(dy[rows])
+    r = rho[rows].astype(np.float64)[:, None]
+    sg = 1.0 / (1.0 + np.exp(-gf))
+    e = df * gf * sg
+    bx = EPS_S * r * (np.abs(w * e) + np.abs(xf) * r * r * np.abs(xf * w * e).sum(1, keepdims=True) / H)
+    bg = EPS_S * np.abs(df * xf * r * w) * sg * (1 + 2 * np.abs(gf))
+    assert _close(to_host_bits(dx.index_select(0, idx)), dx64, bx).all()
+    assert _close(to_host_bits(dg.index_select(0, idx)), dg64, bg).all()
+    # dw over all rows, with its bound sum |e * xhat| accumulated in row blocks
+    _, _, _, _, ref_dw = oracle.gated_bwd_bf16(x, g, dy, w, rho)
+    absum = np.zeros(H)
+    for r0 in range(0, T, 8192):
+        sl = slice(r0, r0 + 8192)
+        gb = oracle.bf16_to_f64(g[sl])
+        eb = oracle.bf16_to_f64(dy[sl]) * gb / (1.0 + np.exp(-gb))
+        absum += np.abs(eb * oracle.bf16_to_f64(x[sl]) * rho[sl].astype(np.float64)[:, None]).sum(0)
+    bw = 1e-4 + 1e-4 * np.abs(ref_dw) + EPS_S * absum
+    assert (np.abs(dw.cpu().numpy().astype(np.float64) - ref_dw) <= bw).all()
+    for _ in range(3):
+        dx2, dg2, dw2 = rn.rmsnorm_gated_bwd(DY, X, G, rstd, W, deterministic=True)
+        assert torch.equal(dx2, dx) and torch.equal(dg2, dg) and torch.equal(dw2, dw)
+    dx3, dg3, dw3 = rn.rmsnorm_gated_bwd(DY, X, G, rstd, W, deterministic=False)
+    assert torch.equal(dx3, dx) and torch.equal(dg3, dg)
+    assert (np.abs(dw3.cpu().numpy().astype(np.float64) - ref_dw) <= bw).all()

@@ -86,3 +86,41 @@ def test_step_replays_bitwise(T, H, wdt, res, route):
         acc_bytes = 256 + ((H * 8 + 255) // 256) * 256
         assert int(ws[:acc_bytes].count_nonzero()) == 0
     print(T, H, wdt, res, route, rep)
+
+
+def test_gated_step_replays_bitwise():
+    # the gated forward / recompute / backward captured once and replayed
+    import rmsnorm_fwd_amd as rn
+    T, H = 1000, 4096
+    x = to_dev_bf16(synth.rows(12, "x", 0, T, H)).view(T, H)
+    g = to_dev_bf16(synth.rows(12, "g", 0, T, H)).view(T, H)
+    dy = to_dev_bf16(synth.rows(12, "dy", 0, T, H)).view(T, H)
+    w = weight_dev(synth.weight(12, H, "f32"))
+    y, dx, dg = torch.empty_like(x), torch.empty_like(x), torch.empty_like(x)
+    rstd = torch.empty(T, dtype=torch.float32, device="cuda")
+    dw = torch.empty(H, dtype=torch.float32, device="cuda")
+    ws = torch.zeros(rn.rmsnorm_bwd_workspace_size(T, 1, H), dtype=torch.uint8, device="cuda")
+
+    def step():
+        rn.rmsnorm_gated_fwd(x, g, w, EPS, y=y, rstd=rstd)
+        rn.rmsnorm_gated_fwd(x, g, w, EPS, y=y, rstd=rstd)
+        rn.rmsnorm_gated_bwd(dy, x, g, rstd, w, dx=dx, dg=dg, dw=dw, workspace=ws)
+
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        step()
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    eager = [t.clone() for t in (y, rstd, dx, dg, dw)]
+    gr = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(gr, stream=s):
+        step()
+    for i in range(3):
+        for t in (y, rstd, dx, dg, dw):
+            t.fill_(0)
+        torch.cuda.synchronize()
+        gr.replay()
+        torch.cuda.synchronize()
+        for a, b in zip(eager, (y, rstd, dx, dg, dw)):
+            assert torch.equal(a, b), f"replay {i} differs"
