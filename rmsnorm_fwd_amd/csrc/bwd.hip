@@ -29,6 +29,11 @@
 //   atomic form: into an FP64 [H] accumulator by atomic add; the workgroup
 //                that draws the last arrival ticket writes dw and zeroes the
 //                accumulator and ticket -- one launch, no waiting.
+//
+// SiLU gate (GATE).  With a gate g the gradient reaching the normalised row
+// is e = dy * silu(g): x*dy*silu(g) is still exact in FP64 (16 + 24 bits),
+// so S, dw and dx follow the same arithmetic with e in place of dy, and the
+// kernel also writes dg = dy * (xhat * w) * silu'(g), formed in FP32.
 #include "device_common.h"
 #include "kernels.h"
 #include "route.h"

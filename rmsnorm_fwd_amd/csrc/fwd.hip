@@ -12,7 +12,8 @@
 // wavefronts).  Relative error of the sum stays below 3 * 2^-24, so rstd is
 // within 2e-7 of the FP64 value before its final FP32 rounding.  The
 // workgroup count is capped and rows are taken grid-stride; results do not
-// depend on the grid.
+// depend on the grid.  With a SiLU gate (GATE) y is further multiplied by
+// silu(g) in FP32.
 #include "device_common.h"
 #include "kernels.h"
 
