@@ -23,6 +23,9 @@ def case():
     y, h, rstd = oracle.fwd_bf16(x, w, 1e-6, r)
     rho32 = rstd.astype(np.float32)
     dx, _, dw = oracle.bwd_bf16(h, dy, w, rho32)
+    g = synth.rows(0, "g", 0, R, H)
+    gy, grstd = oracle.gated_fwd_bf16(x, g, w, 1e-6)
+    gdx, gdg, _, _, gdw = oracle.gated_bwd_bf16(x, g, dy, w, grstd.astype(np.float32))
     return {
         "R": R, "H": H, "eps": 1e-6, "seed": 0,
         "y": [int(v) for v in y.ravel()],
@@ -30,6 +33,13 @@ def case():
         "rstd": [float(v).hex() for v in rstd],
         "dx": [int(v) for v in dx.ravel()],
         "dw": [float(v).hex() for v in dw],
+        "gated": {
+            "y": [int(v) for v in gy.ravel()],
+            "rstd": [float(v).hex() for v in grstd],
+            "dx": [int(v) for v in gdx.ravel()],
+            "dg": [int(v) for v in gdg.ravel()],
+            "dw": [float(v).hex() for v in gdw],
+        },
     }
 
 
