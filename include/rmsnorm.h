@@ -103,7 +103,9 @@ size_t rmsnorm_bwd_workspace_size(int64_t T, int64_t heads, int64_t H, int deter
  * non-deterministic backward keeps between calls (a ticket and an FP64 [H]
  * accumulator).  Every non-deterministic call leaves that part zero again, so
  * this is needed once per fresh allocation (or after a failed call).  A
- * workspace that is all zero bytes is already prepared.
+ * workspace that is all zero bytes is already prepared.  A deterministic
+ * call reads only what it wrote itself earlier in the same call, so it
+ * needs no preparation and leaves the accumulator and ticket as it found them.
  */
 int rmsnorm_bwd_workspace_init(void* workspace, size_t workspace_bytes, int64_t H, void* stream);
 
