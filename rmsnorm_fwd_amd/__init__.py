@@ -158,6 +158,43 @@ def _w_dtype(w):
     raise TypeError("w must be bfloat16 or float32")
 
 
+# The C ABI sees plain pointers: the sizes, dtypes and devices that it cannot
+# check are checked here, before any call into the library.
+
+def _device_of(t, what, device):
+    if not t.is_cuda or t.device != device:
+        raise ValueError(f"{what} must be a GPU tensor on {device}, got {t.device}")
+
+
+def _act(t, what, x):
+    """An activation tensor ([T,H] or [T,heads,H], strides checked apart): BF16, on x's device."""
+    if t is None:
+        return
+    if t.dtype != _torch().bfloat16:
+        raise TypeError(f"{what} must be bfloat16, got {t.dtype}")
+    _device_of(t, what, x.device)
+
+
+def _vec(t, what, n, dtypes, device):
+    """A contiguous [n] vector of one of `dtypes` on `device`."""
+    if t.dtype not in dtypes:
+        raise TypeError(f"{what} must be {' or '.join(str(d) for d in dtypes)}, got {t.dtype}")
+    if t.dim() != 1 or t.numel() != n or not t.is_contiguous():
+        raise ValueError(f"{what} must be a contiguous [{n}] tensor, got shape {tuple(t.shape)}")
+    _device_of(t, what, device)
+
+
+def _weight(w, H, device):
+    torch = _torch()
+    _vec(w, "w", H, (torch.bfloat16, torch.float32), device)
+
+
+def _workspace(ws, device):
+    if not ws.is_contiguous():
+        raise ValueError("workspace must be contiguous")
+    _device_of(ws, "workspace", device)
+
+
 # ------------------------------------------------------------ forward ----
 
 def rmsnorm_fwd(x, w, eps: float = 1e-6, residual=None, deterministic: bool = True, *,
@@ -166,15 +203,21 @@ def rmsnorm_fwd(x, w, eps: float = 1e-6, residual=None, deterministic: bool = Tr
 
     Returns (y, rstd, residual_out); residual_out is None without a residual."""
     torch = _torch()
+    _act(x, "x", x)
     T, heads, H, st, sh = geometry(x)
+    _act(residual, "residual", x)
     _same_geometry(x, residual, "residual")
     y = _like(x) if y is None else y
+    _act(y, "y", x)
     _same_geometry(x, y, "y")
     if residual is not None and residual_out is None:
         residual_out = _like(x)
+    _act(residual_out, "residual_out", x)
     _same_geometry(x, residual_out, "residual_out")
+    _weight(w, H, x.device)
     if rstd is None:
         rstd = torch.empty(T * heads, dtype=torch.float32, device=x.device)
+    _vec(rstd, "rstd", T * heads, (torch.float32,), x.device)
     st_ = lib().rmsnorm_fwd(_ptr(x), _ptr(residual), _ptr(w), _w_dtype(w), _ptr(y),
                             _ptr(residual_out), _ptr(rstd), T, heads, H, st, sh, float(eps),
                             int(bool(deterministic)), _stream(x.device, stream))
@@ -189,6 +232,7 @@ def rmsnorm_bwd_workspace_size(T: int, heads: int, H: int, deterministic: bool =
 
 
 def rmsnorm_bwd_workspace_init(workspace, H: int, stream=None):
+    _workspace(workspace, workspace.device)
     st_ = lib().rmsnorm_bwd_workspace_init(_ptr(workspace), workspace.numel() * workspace.element_size(),
                                            H, _stream(workspace.device, stream))
     _check("rmsnorm_bwd_workspace_init", st_)
@@ -217,13 +261,19 @@ def rmsnorm_bwd_workspace_size_for_route(T: int, heads: int, H: int, route) -> i
 
 def _bwd_args(dy, x, rstd, w, residual, dx, dw):
     torch = _torch()
+    _act(x, "x", x)
     T, heads, H, st, sh = geometry(x)
-    _same_geometry(x, dy, "dy")
-    _same_geometry(x, residual, "residual")
+    for t, what in ((dy, "dy"), (residual, "residual")):
+        _act(t, what, x)
+        _same_geometry(x, t, what)
     dx = _like(x) if dx is None else dx
+    _act(dx, "dx", x)
     _same_geometry(x, dx, "dx")
+    _vec(rstd, "rstd", T * heads, (torch.float32,), x.device)
+    _weight(w, H, x.device)
     if dw is None:
         dw = torch.empty(H, dtype=torch.float32, device=x.device)
+    _vec(dw, "dw", H, (torch.float32,), x.device)
     return (T, heads, H, st, sh), dx, dw
 
 
@@ -236,6 +286,7 @@ def rmsnorm_bwd(dy, x, rstd, w, residual=None, deterministic: bool = True, *,
     (T, heads, H, st, sh), dx, dw = _bwd_args(dy, x, rstd, w, residual, dx, dw)
     if workspace is None:
         workspace = rmsnorm_bwd_workspace(T, heads, H, x.device, deterministic)
+    _workspace(workspace, x.device)
     st_ = lib().rmsnorm_bwd(_ptr(dy), _ptr(x), _ptr(rstd), _ptr(w), _w_dtype(w), _ptr(residual),
                             _ptr(dx), _ptr(dw), _ptr(workspace),
                             workspace.numel() * workspace.element_size(),
@@ -251,6 +302,7 @@ def rmsnorm_bwd_routed(dy, x, rstd, w, route, residual=None, deterministic: bool
     if workspace is None:
         workspace = rmsnorm_bwd_workspace(T, heads, H, x.device, deterministic,
                                           nbytes=rmsnorm_bwd_workspace_size_for_route(T, heads, H, route))
+    _workspace(workspace, x.device)
     st_ = lib().rmsnorm_bwd_routed(_ptr(dy), _ptr(x), _ptr(rstd), _ptr(w), _w_dtype(w), _ptr(residual),
                                    _ptr(dx), _ptr(dw), _ptr(workspace),
                                    workspace.numel() * workspace.element_size(),
@@ -266,12 +318,17 @@ def rmsnorm_gated_fwd(x, g, w, eps: float = 1e-6, deterministic: bool = True, *,
                       stream=None):
     """y = bf16(RMSNorm(x) * w * silu(g)) and rstd.  Returns (y, rstd)."""
     torch = _torch()
+    _act(x, "x", x)
     T, heads, H, st, sh = geometry(x)
+    _act(g, "g", x)
     _same_geometry(x, g, "g")
     y = _like(x) if y is None else y
+    _act(y, "y", x)
     _same_geometry(x, y, "y")
+    _weight(w, H, x.device)
     if rstd is None:
         rstd = torch.empty(T * heads, dtype=torch.float32, device=x.device)
+    _vec(rstd, "rstd", T * heads, (torch.float32,), x.device)
     _check("rmsnorm_gated_fwd", lib().rmsnorm_gated_fwd(
         _ptr(x), _ptr(g), _ptr(w), _w_dtype(w), _ptr(y), _ptr(rstd), T, heads, H, st, sh, float(eps),
         int(bool(deterministic)), _stream(x.device, stream)))
@@ -282,11 +339,14 @@ def rmsnorm_gated_bwd(dy, x, g, rstd, w, deterministic: bool = True, *, dx=None,
                       workspace=None, stream=None):
     """dx, dg (BF16) and dw (FP32) of the gated forward.  Returns (dx, dg, dw)."""
     (T, heads, H, st, sh), dx, dw = _bwd_args(dy, x, rstd, w, None, dx, dw)
+    _act(g, "g", x)
     _same_geometry(x, g, "g")
     dg = _like(x) if dg is None else dg
+    _act(dg, "dg", x)
     _same_geometry(x, dg, "dg")
     if workspace is None:
         workspace = rmsnorm_bwd_workspace(T, heads, H, x.device, deterministic)
+    _workspace(workspace, x.device)
     _check("rmsnorm_gated_bwd", lib().rmsnorm_gated_bwd(
         _ptr(dy), _ptr(x), _ptr(g), _ptr(rstd), _ptr(w), _w_dtype(w), _ptr(dx), _ptr(dg), _ptr(dw),
         _ptr(workspace), workspace.numel() * workspace.element_size(), T, heads, H, st, sh,

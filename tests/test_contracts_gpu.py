@@ -169,3 +169,39 @@ def test_atomic_form_needs_only_its_header_zeroed(H):
     assert all(np.array_equal(dxs[0], d) for d in dxs[1:])
     acc_bytes = 256 + ((H * 8 + 255) // 256) * 256
     assert int(ws[:acc_bytes].count_nonzero()) == 0, "atomic form did not leave its header zero"
+
+
+def test_binding_rejects_what_the_abi_cannot_check():
+    """Lengths, contiguity and dtypes of the vectors (rstd, w, dw), the
+    activations' dtype and the workspace layout are checked in the binding
+    before any launch; nothing is enqueued for a rejected call."""
+    import torch
+    import rmsnorm_fwd_amd as rn
+    T, H = 16, 512
+    x = torch.randn(T, H, device="cuda").bfloat16()
+    w = torch.ones(H, device="cuda")
+    y, rstd, _ = rn.rmsnorm_fwd(x, w)
+    bad = [
+        (ValueError, "rstd must be a contiguous", lambda: rn.rmsnorm_fwd(x, w, rstd=torch.empty(T - 1, device="cuda"))),
+        (ValueError, "w must be a contiguous", lambda: rn.rmsnorm_fwd(x, torch.ones(H - 8, device="cuda"))),
+        (ValueError, "w must be a contiguous", lambda: rn.rmsnorm_fwd(x, torch.ones(2 * H, device="cuda")[::2])),
+        (TypeError, "w must be", lambda: rn.rmsnorm_fwd(x, w.half())),
+        (TypeError, "y must be bfloat16", lambda: rn.rmsnorm_fwd(x, w, y=torch.empty(T, H, device="cuda"))),
+        (TypeError, "dy must be bfloat16", lambda: rn.rmsnorm_bwd(x.float(), x, rstd, w)),
+        (ValueError, "rstd must be a contiguous", lambda: rn.rmsnorm_bwd(x, x, rstd[:-1], w)),
+        (TypeError, "dw must be", lambda: rn.rmsnorm_bwd(x, x, rstd, w, dw=torch.empty(H, device="cuda").half())),
+        (ValueError, "dw must be a contiguous", lambda: rn.rmsnorm_bwd(x, x, rstd, w, dw=torch.empty(H + 8, device="cuda"))),
+        (ValueError, "workspace must be contiguous",
+         lambda: rn.rmsnorm_bwd(x, x, rstd, w, workspace=torch.zeros(2 << 20, dtype=torch.uint8, device="cuda")[::2])),
+        (TypeError, "g must be bfloat16", lambda: rn.rmsnorm_gated_fwd(x, x.float(), w)),
+        (TypeError, "dg must be bfloat16",
+         lambda: rn.rmsnorm_gated_bwd(x, x, x, rstd, w, dg=torch.empty(T, H, device="cuda"))),
+    ]
+    for exc, msg, call in bad:
+        with pytest.raises(exc, match=msg):
+            call()
+    torch.cuda.synchronize()
+    # the good call still works after the rejected ones
+    dx, dw = rn.rmsnorm_bwd(x, x, rstd, w)
+    torch.cuda.synchronize()
+    assert torch.isfinite(dw).all()
