@@ -205,3 +205,29 @@ def test_binding_rejects_what_the_abi_cannot_check():
     dx, dw = rn.rmsnorm_bwd(x, x, rstd, w)
     torch.cuda.synchronize()
     assert torch.isfinite(dw).all()
+
+
+@pytest.mark.parametrize("T,H", [(64, 1536), (4, 4096), (1000, 256)])
+def test_non_finite_rows_stay_in_their_rows(T, H):
+    """NaN and Inf inputs propagate by IEEE rules within their own row only:
+    every other row's y, rstd and dx are bitwise those of the clean input
+    (dw sums over rows, so its affected columns are not compared)."""
+    import torch
+    import rmsnorm_fwd_amd as rn
+    g = torch.Generator().manual_seed(T + H)
+    x = torch.randn(T, H, generator=g).bfloat16().cuda()
+    dy = torch.randn(T, H, generator=g).bfloat16().cuda()
+    w = (1 + 0.1 * torch.randn(H, generator=g)).cuda()
+    bad = x.clone()
+    bad[1, 3] = float("nan")
+    bad[T - 1, 0] = float("inf")
+    keep = torch.ones(T, dtype=torch.bool, device="cuda")
+    keep[1] = keep[T - 1] = False
+    y0, r0, _ = rn.rmsnorm_fwd(x, w)
+    y1, r1, _ = rn.rmsnorm_fwd(bad, w)
+    dx0, _ = rn.rmsnorm_bwd(dy, x, r0, w)
+    dx1, _ = rn.rmsnorm_bwd(dy, bad, r1, w)
+    torch.cuda.synchronize()
+    assert torch.equal(y0[keep], y1[keep]) and torch.equal(r0[keep], r1[keep])
+    assert torch.equal(dx0[keep], dx1[keep])
+    assert torch.isnan(r1[1]) and torch.isnan(y1[1]).all()
