@@ -1,0 +1,276 @@
+// Host check of the C-ABI layer (api.cpp, route.cpp), built for the host with
+// AddressSanitizer and UBSan.  The kernel launchers are replaced by stubs that
+// record what they would launch, and the two HIP queries api.cpp makes are
+// stubbed too, so no GPU and no HIP runtime is involved.  Pointers are
+// addresses in a host array that the ABI layer never dereferences.
+//
+// Checked:
+//   * every error path returns its status before any launch;
+//   * for a sweep of shapes, the backward's workspace accesses (ticket,
+//     FP64 accumulator, chunk partials) stay inside rmsnorm_bwd_workspace_size,
+//     one byte less is refused, and the launch parameters are in range;
+//   * the forward grid is within [1, compute units * layout cap] and every
+//     launch gets the row count and width it was given.
+// Prints "ok" and exits 0, or prints the first failures and exits 1.
+#include <cmath>
+#include <cstdint>
+#include <cstdio>
+#include <cstring>
+
+#include "../../include/rmsnorm.h"
+#include "kernels.h"
+#include "layouts.h"
+#include "route.h"
+
+namespace rmsn {
+
+struct Calls {
+    int fwd = 0, bwd = 0, reduce = 0, fill = 0;
+    FwdParams fp{};
+    BwdParams bp{};
+    int grid = 0, layout = -1, reduce_chunks = 0, reduce_h = 0;
+    int64_t fill_bytes = 0;
+    const void* fill_ptr = nullptr;
+};
+static Calls g;
+
+hipError_t launch_fwd(int layout, bool, const FwdParams& p, int grid, hipStream_t)
+{
+    ++g.fwd;
+    g.fp = p;
+    g.grid = grid;
+    g.layout = layout;
+    return hipSuccess;
+}
+hipError_t launch_bwd(int layout, bool, const BwdParams& p, hipStream_t)
+{
+    ++g.bwd;
+    g.bp = p;
+    g.layout = layout;
+    return hipSuccess;
+}
+hipError_t launch_dw_reduce(const double*, int chunks, int H, float*, hipStream_t)
+{
+    ++g.reduce;
+    g.reduce_chunks = chunks;
+    g.reduce_h = H;
+    return hipSuccess;
+}
+hipError_t launch_fill_zero(void* ptr, int64_t bytes, hipStream_t)
+{
+    ++g.fill;
+    g.fill_ptr = ptr;
+    g.fill_bytes = bytes;
+    return hipSuccess;
+}
+
+}  // namespace rmsn
+
+// the two device queries api.cpp makes (compute-unit count for the forward grid)
+extern "C" hipError_t hipGetDevice(int* d)
+{
+    *d = 0;
+    return hipSuccess;
+}
+extern "C" hipError_t hipDeviceGetAttribute(int* v, hipDeviceAttribute_t, int)
+{
+    *v = 256;
+    return hipSuccess;
+}
+
+using namespace rmsn;
+
+static long fails = 0;
+#define CHECK(c, ...)                                   \
+    do {                                                \
+        if (!(c)) {                                     \
+            if (fails < 20) {                           \
+                std::printf("%s:%d: ", __FILE__, __LINE__); \
+                std::printf(__VA_ARGS__);               \
+                std::printf("\n");                      \
+            }                                           \
+            ++fails;                                    \
+        }                                               \
+    } while (0)
+
+alignas(256) static char mem[16][1024];
+static void* P(int i) { return mem[i]; }
+
+static void reset() { g = Calls{}; }
+
+static int bwd(int64_t T, int64_t heads, int64_t H, size_t ws_bytes, int det, const void* dres = nullptr,
+               int64_t st = -1, int64_t sh = -1)
+{
+    if (sh < 0) sh = H;
+    if (st < 0) st = heads * sh;
+    return rmsnorm_bwd(P(0), P(1), (const float*)P(2), P(3), RMSN_W_F32, dres, P(4), (float*)P(5), P(6), ws_bytes,
+                       T, heads, H, st, sh, det, nullptr);
+}
+
+static void check_error_paths()
+{
+    const int64_t H = 512;
+    float* rstd = (float*)P(2);
+    // forward
+    reset();
+    CHECK(rmsnorm_fwd(P(0), nullptr, P(1), RMSN_W_BF16, P(2), nullptr, rstd, 4, 1, 7, 7, 7, 1e-6, 1, nullptr) ==
+              RMSN_ERR_UNSUPPORTED, "H = 7");
+    CHECK(rmsnorm_fwd(P(0), nullptr, P(1), RMSN_W_BF16, P(2), nullptr, rstd, 4, 1, RMSN_MAX_H + 8, RMSN_MAX_H + 8,
+                      RMSN_MAX_H + 8, 1e-6, 1, nullptr) == RMSN_ERR_UNSUPPORTED, "H too large");
+    CHECK(rmsnorm_fwd(P(0), nullptr, P(1), RMSN_W_BF16, P(2), nullptr, rstd, -1, 1, H, H, H, 1e-6, 1, nullptr) ==
+              RMSN_ERR_INVALID_ARG, "T < 0");
+    CHECK(rmsnorm_fwd(P(0), nullptr, P(1), RMSN_W_BF16, P(2), nullptr, rstd, 4, 0, H, H, H, 1e-6, 1, nullptr) ==
+              RMSN_ERR_INVALID_ARG, "heads = 0");
+    CHECK(rmsnorm_fwd(P(0), nullptr, P(1), RMSN_W_BF16, P(2), nullptr, rstd, 4, 1, H, H - 8, H, 1e-6, 1, nullptr) ==
+              RMSN_ERR_INVALID_ARG, "overlapping rows");
+    CHECK(rmsnorm_fwd(P(0), nullptr, P(1), RMSN_W_BF16, P(2), nullptr, rstd, 4, 2, H, 2 * H - 8, H, 1e-6, 1,
+                      nullptr) == RMSN_ERR_INVALID_ARG, "overlapping tokens");
+    CHECK(rmsnorm_fwd(P(0), nullptr, P(1), RMSN_W_BF16, P(2), nullptr, rstd, 4, 1, H, H + 4, H, 1e-6, 1, nullptr) ==
+              RMSN_ERR_MISALIGNED, "stride not a multiple of 8");
+    CHECK(rmsnorm_fwd((char*)P(0) + 2, nullptr, P(1), RMSN_W_BF16, P(2), nullptr, rstd, 4, 1, H, H, H, 1e-6, 1,
+                      nullptr) == RMSN_ERR_MISALIGNED, "misaligned x");
+    CHECK(rmsnorm_fwd(P(0), nullptr, P(1), RMSN_W_BF16, P(2), nullptr, rstd, 4, 1, H, H, H, NAN, 1, nullptr) ==
+              RMSN_ERR_INVALID_ARG, "eps NaN");
+    CHECK(rmsnorm_fwd(P(0), nullptr, P(1), RMSN_W_BF16, P(2), nullptr, rstd, 4, 1, H, H, H, -1.0, 1, nullptr) ==
+              RMSN_ERR_INVALID_ARG, "eps < 0");
+    CHECK(rmsnorm_fwd(P(0), nullptr, P(1), 2, P(2), nullptr, rstd, 4, 1, H, H, H, 1e-6, 1, nullptr) ==
+              RMSN_ERR_INVALID_ARG, "w dtype");
+    CHECK(rmsnorm_fwd(P(0), P(3), P(1), RMSN_W_BF16, P(2), nullptr, rstd, 4, 1, H, H, H, 1e-6, 1, nullptr) ==
+              RMSN_ERR_INVALID_ARG, "residual without residual_out");
+    CHECK(rmsnorm_fwd(nullptr, nullptr, P(1), RMSN_W_BF16, P(2), nullptr, rstd, 4, 1, H, H, H, 1e-6, 1, nullptr) ==
+              RMSN_ERR_INVALID_ARG, "x null");
+    CHECK(rmsnorm_fwd(P(0), nullptr, P(1), RMSN_W_BF16, P(2), nullptr, rstd, INT64_MAX, 1, H, H, H, 1e-6, 1,
+                      nullptr) == RMSN_ERR_INVALID_ARG, "T huge");
+    CHECK(rmsnorm_fwd(P(0), nullptr, P(1), RMSN_W_BF16, P(2), nullptr, rstd, INT64_MAX / 2, 4, H, 4 * H, H, 1e-6, 1,
+                      nullptr) == RMSN_ERR_INVALID_ARG, "T * heads overflows");
+    CHECK(rmsnorm_fwd(P(0), nullptr, P(1), RMSN_W_BF16, P(2), nullptr, rstd, int64_t(1) << 30, 1, H, H, H, 1e-6, 1,
+                      nullptr) == RMSN_ERR_INVALID_ARG, "R = 2^30");
+    CHECK(rmsnorm_gated_fwd(P(0), nullptr, P(1), RMSN_W_BF16, P(2), rstd, 4, 1, H, H, H, 1e-6, 1, nullptr) ==
+              RMSN_ERR_INVALID_ARG, "gate null");
+    CHECK(rmsnorm_gated_fwd(P(0), (char*)P(3) + 8, P(1), RMSN_W_BF16, P(2), rstd, 4, 1, H, H, H, 1e-6, 1,
+                            nullptr) == RMSN_ERR_MISALIGNED, "gate misaligned");
+    CHECK(g.fwd == 0, "a rejected forward launched");
+
+    // backward
+    const size_t ws = rmsnorm_bwd_workspace_size(64, 1, H, 1);
+    reset();
+    CHECK(bwd(64, 1, H, ws - 1, 1) == RMSN_ERR_WORKSPACE, "workspace one byte short");
+    CHECK(rmsnorm_bwd(P(0), P(1), (const float*)P(2), P(3), RMSN_W_F32, nullptr, P(4), (float*)P(5),
+                      (char*)P(6) + 128, ws, 64, 1, H, H, H, 1, nullptr) == RMSN_ERR_MISALIGNED,
+          "workspace misaligned");
+    CHECK(rmsnorm_bwd(P(0), P(1), (const float*)P(2), P(3), RMSN_W_F32, nullptr, P(4), nullptr, P(6), ws, 64, 1, H,
+                      H, H, 1, nullptr) == RMSN_ERR_INVALID_ARG, "dw null");
+    CHECK(rmsnorm_bwd(P(0), P(1), (const float*)((char*)P(2) + 2), P(3), RMSN_W_F32, nullptr, P(4), (float*)P(5),
+                      P(6), ws, 64, 1, H, H, H, 1, nullptr) == RMSN_ERR_MISALIGNED, "rstd misaligned");
+    CHECK(rmsnorm_bwd(P(0), P(1), (const float*)P(2), P(3), RMSN_W_F32, (char*)P(7) + 8, P(4), (float*)P(5), P(6),
+                      ws, 64, 1, H, H, H, 1, nullptr) == RMSN_ERR_MISALIGNED, "dres misaligned");
+    const rmsn_route atomic{RMSN_FORM_ATOMIC, 8}, zero{RMSN_FORM_PAIR, 0}, many{RMSN_FORM_PAIR, 65537},
+        bad_form{7, 8};
+    for (const rmsn_route& r : {zero, many, bad_form})
+        CHECK(rmsnorm_bwd_routed(P(0), P(1), (const float*)P(2), P(3), RMSN_W_F32, nullptr, P(4), (float*)P(5), P(6),
+                                 ws, 64, 1, H, H, H, 0, r, nullptr) == RMSN_ERR_INVALID_ARG,
+              "route (%d, %d)", r.form, r.chunks);
+    CHECK(rmsnorm_bwd_routed(P(0), P(1), (const float*)P(2), P(3), RMSN_W_F32, nullptr, P(4), (float*)P(5), P(6), ws,
+                             64, 1, H, H, H, 1, atomic, nullptr) == RMSN_ERR_INVALID_ARG,
+          "deterministic atomic route");
+    CHECK(rmsnorm_gated_bwd(P(0), P(1), nullptr, (const float*)P(2), P(3), RMSN_W_F32, P(4), P(7), (float*)P(5),
+                            P(6), ws, 64, 1, H, H, H, 1, nullptr) == RMSN_ERR_INVALID_ARG, "gate null");
+    CHECK(rmsnorm_gated_bwd(P(0), P(1), P(8), (const float*)P(2), P(3), RMSN_W_F32, P(4), (char*)P(7) + 4,
+                            (float*)P(5), P(6), ws, 64, 1, H, H, H, 1, nullptr) == RMSN_ERR_MISALIGNED,
+          "dgate misaligned");
+    CHECK(rmsnorm_bwd_workspace_init(P(6), ws, 12, nullptr) == RMSN_ERR_INVALID_ARG, "init H = 12");
+    CHECK(rmsnorm_bwd_workspace_init(P(6), 100, H, nullptr) == RMSN_ERR_WORKSPACE, "init too small");
+    CHECK(g.bwd == 0 && g.reduce == 0 && g.fill == 0, "a rejected backward launched");
+    CHECK(rmsnorm_bwd_workspace_size(4, 1, 12, 1) == 0 && rmsnorm_bwd_workspace_size(-1, 1, H, 1) == 0 &&
+              rmsnorm_bwd_workspace_size(int64_t(1) << 30, 1, H, 1) == 0,
+          "workspace size of an invalid shape is not 0");
+
+    // R = 0: the backward zero-fills dw and launches nothing else
+    reset();
+    CHECK(bwd(0, 1, H, 0, 1) == RMSN_OK && g.fill == 1 && g.fill_bytes == H * 4 && g.bwd == 0,
+          "R = 0 backward");
+    reset();
+    CHECK(rmsnorm_fwd(P(0), nullptr, P(1), RMSN_W_BF16, P(2), nullptr, rstd, 0, 1, H, H, H, 1e-6, 1, nullptr) ==
+              RMSN_OK && g.fwd == 0, "R = 0 forward");
+
+    for (int s = -1; s <= 6; ++s) CHECK(rmsnorm_status_string(s) != nullptr, "status string %d", s);
+}
+
+// One backward call at (T, heads, H) in both modes: bounds of every
+// workspace access, launch parameters, and the one-byte-short refusal.
+static void check_backward_shape(int64_t T, int64_t heads, int64_t H)
+{
+    const int64_t R = T * heads;
+    for (int det = 0; det <= 1; ++det) {
+        const size_t ws = rmsnorm_bwd_workspace_size(T, heads, H, det);
+        CHECK(ws > 0, "workspace size 0 for T=%lld heads=%lld H=%lld", (long long)T, (long long)heads, (long long)H);
+        reset();
+        const int st = bwd(T, heads, H, ws, det);
+        CHECK(st == RMSN_OK, "status %d for T=%lld heads=%lld H=%lld", st, (long long)T, (long long)heads,
+              (long long)H);
+        if (st != RMSN_OK || R == 0) continue;
+        const BwdParams& p = g.bp;
+        const char* base = (const char*)P(6);
+        CHECK(g.bwd == 1 && p.R == R && p.H == H, "launch R/H");
+        CHECK(p.chunks >= 1 && p.chunks <= kMaxChunks, "chunks %d", p.chunks);
+        CHECK(p.form == FORM_PAIR, "default route is the pair");
+        CHECK((const char*)p.ticket == base && (const char*)p.acc >= base + sizeof(unsigned),
+              "ticket/accumulator placement");
+        CHECK((size_t)((const char*)p.acc - base) + (size_t)H * 8 <= ws, "accumulator past the workspace");
+        CHECK((size_t)((const char*)p.acc - base) % 8 == 0 && (size_t)((const char*)p.part - base) % 16 == 0,
+              "workspace alignment");
+        if (p.chunks > 1) {
+            CHECK(!p.direct_dw && g.reduce == 1 && g.reduce_chunks == p.chunks && g.reduce_h == H,
+                  "pair launches its reduce");
+            CHECK((size_t)((const char*)p.part - base) + (size_t)p.chunks * H * 8 <= ws,
+                  "partials past the workspace: T=%lld heads=%lld H=%lld chunks=%d", (long long)T,
+                  (long long)heads, (long long)H, p.chunks);
+        } else {
+            CHECK(p.direct_dw && g.reduce == 0, "one chunk writes dw itself");
+        }
+        const size_t need = ws_bytes_for(R, H, BwdRoute{p.form, p.chunks});
+        reset();
+        CHECK(bwd(T, heads, H, need - 1, det) == RMSN_ERR_WORKSPACE && g.bwd == 0,
+              "a workspace one byte short is refused");
+    }
+}
+
+static void check_forward_shape(int64_t T, int64_t heads, int64_t H)
+{
+    reset();
+    const int st = rmsnorm_fwd(P(0), nullptr, P(1), RMSN_W_BF16, P(2), nullptr, (float*)P(3), T, heads, H,
+                               heads * H, H, 1e-6, 1, nullptr);
+    CHECK(st == RMSN_OK, "forward status %d", st);
+    if (T * heads == 0) return;
+    const Layout& L = kFwdLayouts[g.layout];
+    CHECK(H <= L.max_h && (g.layout == 0 || H > kFwdLayouts[g.layout - 1].max_h), "forward layout for H=%lld",
+          (long long)H);
+    CHECK(g.grid >= 1 && g.grid <= 256 * L.k, "forward grid %d", g.grid);
+    CHECK(g.fp.R == T * heads && g.fp.H == H, "forward R/H");
+}
+
+int main()
+{
+    check_error_paths();
+    const int64_t Ts[] = {1, 2, 3, 4, 5, 7, 16, 63, 64, 65, 255, 256, 257, 1000, 1024, 4096, 4099,
+                          16384, 65536, 131072, 1 << 20, (int64_t(1) << 30) - 1};
+    for (int64_t H = 8; H <= RMSN_MAX_H; H += (H < 1024 ? 8 : (H < 8192 ? 72 : 520))) {
+        for (int64_t T : Ts) {
+            check_backward_shape(T, 1, H);
+            check_forward_shape(T, 1, H);
+        }
+    }
+    for (int64_t H : {int64_t(8), int64_t(256), int64_t(1536), int64_t(4096), int64_t(6144), int64_t(16384)})
+        for (int64_t heads : {int64_t(2), int64_t(3), int64_t(24), int64_t(1000)})
+            for (int64_t T : {int64_t(1), int64_t(5), int64_t(4097), int64_t(32768), ((int64_t(1) << 30) - 1) / 1000}) {
+                if (T * heads >= (int64_t(1) << 30)) continue;
+                check_backward_shape(T, heads, H);
+                check_forward_shape(T, heads, H);
+            }
+    if (fails) {
+        std::printf("%ld failures\n", fails);
+        return 1;
+    }
+    std::printf("ok\n");
+    return 0;
+}

@@ -160,6 +160,35 @@ def test_row_map_division_is_exact(tmp_path):
     assert " 0 failures" in out.stdout
 
 
+# Host code under AddressSanitizer and UBSan (the GPU code is not built with
+# sanitizers; these drivers need neither a GPU nor the HIP runtime).
+SANITIZE = ["-O1", "-g", "-fsanitize=address,undefined", "-fno-sanitize-recover=all"]
+
+
+def test_abi_layer_under_sanitizers(tmp_path):
+    """api.cpp and route.cpp with stub launchers: every error path, and for a
+    sweep of shapes every workspace access inside rmsnorm_bwd_workspace_size."""
+    csrc = os.path.join(ROOT, "rmsnorm_fwd_amd", "csrc")
+    exe = str(tmp_path / "abi_check")
+    subprocess.run(["g++", "-std=c++17", *SANITIZE, "-D__HIP_PLATFORM_AMD__", "-I/opt/rocm/include",
+                    f"-I{os.path.join(ROOT, 'include')}", f"-I{csrc}",
+                    os.path.join(ROOT, "tests", "host", "abi_check.cpp"), os.path.join(csrc, "api.cpp"),
+                    os.path.join(csrc, "route.cpp"), "-o", exe], check=True)
+    out = subprocess.run([exe], capture_output=True, text=True)
+    assert out.returncode == 0 and out.stdout.strip().endswith("ok"), out.stdout + out.stderr
+
+
+def test_oracle_under_sanitizers(tmp_path):
+    """Every exported oracle function on small and edge shapes, buffers of
+    exact size."""
+    exe = str(tmp_path / "oracle_check")
+    subprocess.run(["gcc", "-std=c11", *SANITIZE, "-fopenmp", "-ffp-contract=off",
+                    os.path.join(ROOT, "tests", "host", "oracle_check.c"), os.path.join(ROOT, "oracle", "oracle.c"),
+                    "-lm", "-o", exe], check=True)
+    out = subprocess.run([exe], capture_output=True, text=True, env={**os.environ, "OMP_NUM_THREADS": "4"})
+    assert out.returncode == 0 and out.stdout.strip().endswith("ok"), out.stdout + out.stderr
+
+
 def test_route_chunk_count_grows_with_rows_and_stays_bounded():
     # one workgroup per chunk: never more than 512 (two per compute unit), one
     # for the smallest inputs, and never fewer as the row count grows
