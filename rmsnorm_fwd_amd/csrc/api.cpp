@@ -141,8 +141,9 @@ int fwd_impl(const void* x, const void* residual, const void* gate, const void* 
         (residual && (!aligned(residual, 16) || !aligned(residual_out, 16))) || (gate && !aligned(gate, 16)))
         return RMSN_ERR_MISALIGNED;
 
-    const int layout = pick_layout(kFwdLayouts, kNumFwdLayouts, s.H);
-    const Layout& L = kFwdLayouts[layout];
+    const Layout* table = residual ? kFwdResLayouts : kFwdLayouts;
+    const int layout = pick_layout(table, kNumFwdLayouts, s.H);
+    const Layout& L = table[layout];
     const int64_t rpi = (int64_t)slots_of(L.lpr) * L.u;
     const int64_t iters = (s.R + rpi - 1) / rpi;
     const int64_t cap = (int64_t)cu_count() * L.k;

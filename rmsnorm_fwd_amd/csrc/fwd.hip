@@ -165,13 +165,22 @@ static hipError_t fwd_w(bool w_f32, const FwdParams& p, int grid, hipStream_t s)
 template <int LPR, int V, int U>
 static hipError_t fwd_dispatch(bool w_f32, const FwdParams& p, int grid, hipStream_t s)
 {
-    if (p.r) return fwd_w<LPR, V, U, true, false>(w_f32, p, grid, s);
     if (p.g) return fwd_w<LPR, V, U, false, true>(w_f32, p, grid, s);
     return fwd_w<LPR, V, U, false, false>(w_f32, p, grid, s);
 }
 
+// `layout` indexes the residual table when p.r is set, else the plain one.
 hipError_t launch_fwd(int layout, bool w_f32, const FwdParams& p, int grid, hipStream_t s)
 {
+    if (p.r) {
+        switch (layout) {
+#define RMSN_FWD_RES_CASE(id, mh, l, vv, uu, kk) \
+    case id: return fwd_w<l, vv, uu, true, false>(w_f32, p, grid, s);
+            RMSN_FWD_RES_LAYOUTS(RMSN_FWD_RES_CASE)
+#undef RMSN_FWD_RES_CASE
+        default: return hipErrorInvalidValue;
+        }
+    }
     switch (layout) {
 #define RMSN_FWD_CASE(id, mh, l, vv, uu, kk) \
     case id: return fwd_dispatch<l, vv, uu>(w_f32, p, grid, s);

@@ -67,6 +67,7 @@ struct BwdParams {
 };
 
 // Launchers; return the launch's hipError_t.
+// launch_fwd: `layout` indexes kFwdResLayouts when p.r is set, else kFwdLayouts.
 hipError_t launch_fwd(int layout, bool w_f32, const FwdParams& p, int grid, hipStream_t s);
 hipError_t launch_bwd(int layout, bool w_f32, const BwdParams& p, hipStream_t s);
 hipError_t launch_dw_reduce(const double* part, int chunks, int H, float* dw, hipStream_t s);

@@ -28,7 +28,7 @@ struct Layout {
 // X(id, max_h, lpr, v, u, k); max_h == lpr * v * 8.  Every entry was picked
 // by timing the candidates on MI355X with cold caches (T*H between 2^25 and
 // 2^30 elements); the smallest max_h >= H serves H.  A tuning build may
-// supply its own candidate tables through RMSN_LAYOUTS_OVERRIDE.
+// supply its own candidate tables (all three) through RMSN_LAYOUTS_OVERRIDE.
 #ifdef RMSN_LAYOUTS_OVERRIDE
 #include RMSN_LAYOUTS_OVERRIDE
 #else
@@ -45,6 +45,30 @@ struct Layout {
     X(9, 5120, 320, 2, 2, 32)  \
     X(10, 6144, 768, 1, 2, 24) \
     X(11, 8192, 512, 2, 2, 32) \
+    X(12, 16384, 512, 4, 1, 8)
+
+// The forward with a fused residual add streams four tensors (x, r in; h, y
+// out) instead of two.  It keeps the plain forward's lanes and vectors per
+// row for every width -- so its row sums, rstd and y are the plain forward's
+// bits for the same input h -- and differs only in rows per iteration and
+// grid cap where that was faster: at H 5120 and 6144 four rows per row group
+// and iteration keep twice the loads in flight (T 131072, H 6144: 1183 ->
+// 1104 us; T 65536, H 5120: 497 -> 475 us; the grid cap made no difference
+// between 8 and 32 workgroups per compute unit).  At H 4096 four rows were
+// slower (372 -> 386 us), so the plain layout stays there and below.
+#define RMSN_FWD_RES_LAYOUTS(X) \
+    X(0, 64, 8, 1, 4, 64)       \
+    X(1, 128, 16, 1, 4, 64)     \
+    X(2, 256, 8, 4, 1, 64)      \
+    X(3, 512, 32, 2, 2, 64)     \
+    X(4, 1024, 32, 4, 1, 64)    \
+    X(5, 1536, 32, 6, 1, 16)    \
+    X(6, 2048, 256, 1, 4, 32)   \
+    X(7, 3072, 64, 6, 1, 32)    \
+    X(8, 4096, 512, 1, 2, 32)   \
+    X(9, 5120, 320, 2, 4, 16)   \
+    X(10, 6144, 768, 1, 4, 16)  \
+    X(11, 8192, 512, 2, 2, 32)  \
     X(12, 16384, 512, 4, 1, 8)
 
 #define RMSN_BWD_LAYOUTS(X)       \
@@ -64,6 +88,7 @@ struct Layout {
 
 #define RMSN_CHECK_LAYOUT(id, mh, l, vv, uu, kk) static_assert((mh) == (l) * (vv) * 8, "layout width");
 RMSN_FWD_LAYOUTS(RMSN_CHECK_LAYOUT)
+RMSN_FWD_RES_LAYOUTS(RMSN_CHECK_LAYOUT)
 RMSN_BWD_LAYOUTS(RMSN_CHECK_LAYOUT)
 #undef RMSN_CHECK_LAYOUT
 
@@ -80,10 +105,21 @@ RMSN_BWD_LAYOUTS(RMSN_CHECK_LDS)
 
 #define RMSN_LAYOUT_ENTRY(id, mh, l, vv, uu, kk) Layout{mh, l, vv, uu, kk},
 static constexpr Layout kFwdLayouts[] = {RMSN_FWD_LAYOUTS(RMSN_LAYOUT_ENTRY)};
+static constexpr Layout kFwdResLayouts[] = {RMSN_FWD_RES_LAYOUTS(RMSN_LAYOUT_ENTRY)};
 static constexpr Layout kBwdLayouts[] = {RMSN_BWD_LAYOUTS(RMSN_LAYOUT_ENTRY)};
 #undef RMSN_LAYOUT_ENTRY
 
 static constexpr int kNumFwdLayouts = sizeof(kFwdLayouts) / sizeof(kFwdLayouts[0]);
+static_assert(sizeof(kFwdResLayouts) == sizeof(kFwdLayouts), "one residual layout per forward layout");
+
+// Same widths, lanes and vectors per row in both forward tables.
+constexpr bool fwd_tables_agree(int i = 0)
+{
+    return i == kNumFwdLayouts ||
+           (kFwdResLayouts[i].max_h == kFwdLayouts[i].max_h && kFwdResLayouts[i].lpr == kFwdLayouts[i].lpr &&
+            kFwdResLayouts[i].v == kFwdLayouts[i].v && fwd_tables_agree(i + 1));
+}
+static_assert(fwd_tables_agree(), "the residual forward keeps the plain forward's row layout");
 static constexpr int kNumBwdLayouts = sizeof(kBwdLayouts) / sizeof(kBwdLayouts[0]);
 
 // Workgroup size: the largest multiple of LPR not above 256, or LPR itself

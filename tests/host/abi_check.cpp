@@ -235,18 +235,20 @@ static void check_backward_shape(int64_t T, int64_t heads, int64_t H)
     }
 }
 
-static void check_forward_shape(int64_t T, int64_t heads, int64_t H)
+static void check_forward_shape(int64_t T, int64_t heads, int64_t H, bool residual)
 {
     reset();
-    const int st = rmsnorm_fwd(P(0), nullptr, P(1), RMSN_W_BF16, P(2), nullptr, (float*)P(3), T, heads, H,
-                               heads * H, H, 1e-6, 1, nullptr);
+    const int st = rmsnorm_fwd(P(0), residual ? P(4) : nullptr, P(1), RMSN_W_BF16, P(2), residual ? P(5) : nullptr,
+                               (float*)P(3), T, heads, H, heads * H, H, 1e-6, 1, nullptr);
     CHECK(st == RMSN_OK, "forward status %d", st);
     if (T * heads == 0) return;
-    const Layout& L = kFwdLayouts[g.layout];
-    CHECK(H <= L.max_h && (g.layout == 0 || H > kFwdLayouts[g.layout - 1].max_h), "forward layout for H=%lld",
+    const Layout* table = residual ? kFwdResLayouts : kFwdLayouts;
+    const Layout& L = table[g.layout];
+    CHECK(H <= L.max_h && (g.layout == 0 || H > table[g.layout - 1].max_h), "forward layout for H=%lld",
           (long long)H);
     CHECK(g.grid >= 1 && g.grid <= 256 * L.k, "forward grid %d", g.grid);
     CHECK(g.fp.R == T * heads && g.fp.H == H, "forward R/H");
+    CHECK((g.fp.r != nullptr) == residual && (g.fp.h != nullptr) == residual, "forward residual pointers");
 }
 
 int main()
@@ -257,7 +259,8 @@ int main()
     for (int64_t H = 8; H <= RMSN_MAX_H; H += (H < 1024 ? 8 : (H < 8192 ? 72 : 520))) {
         for (int64_t T : Ts) {
             check_backward_shape(T, 1, H);
-            check_forward_shape(T, 1, H);
+            check_forward_shape(T, 1, H, false);
+            check_forward_shape(T, 1, H, true);
         }
     }
     for (int64_t H : {int64_t(8), int64_t(256), int64_t(1536), int64_t(4096), int64_t(6144), int64_t(16384)})
@@ -265,7 +268,8 @@ int main()
             for (int64_t T : {int64_t(1), int64_t(5), int64_t(4097), int64_t(32768), ((int64_t(1) << 30) - 1) / 1000}) {
                 if (T * heads >= (int64_t(1) << 30)) continue;
                 check_backward_shape(T, heads, H);
-                check_forward_shape(T, heads, H);
+                check_forward_shape(T, heads, H, false);
+                check_forward_shape(T, heads, H, true);
             }
     if (fails) {
         std::printf("%ld failures\n", fails);
