@@ -141,7 +141,8 @@ int fwd_impl(const void* x, const void* residual, const void* gate, const void* 
         (residual && (!aligned(residual, 16) || !aligned(residual_out, 16))) || (gate && !aligned(gate, 16)))
         return RMSN_ERR_MISALIGNED;
 
-    const Layout* table = residual ? kFwdResLayouts : kFwdLayouts;
+    const int kind = fwd_table_kind(s.R, residual != nullptr, gate != nullptr);
+    const Layout* table = fwd_table(kind);
     const int layout = pick_layout(table, kNumFwdLayouts, s.H);
     const Layout& L = table[layout];
     const int64_t rpi = (int64_t)slots_of(L.lpr) * L.u;
@@ -162,7 +163,7 @@ int fwd_impl(const void* x, const void* residual, const void* gate, const void* 
     p.H = (int)s.H;
     p.eps = eps;
     p.inv_h = 1.0 / (double)s.H;
-    return status_of(launch_fwd(layout, w_dtype == RMSN_W_F32, p, grid, static_cast<hipStream_t>(stream)));
+    return status_of(launch_fwd(kind, layout, w_dtype == RMSN_W_F32, p, grid, static_cast<hipStream_t>(stream)));
 }
 
 }  // namespace

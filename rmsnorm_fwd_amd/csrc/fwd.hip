@@ -169,10 +169,19 @@ static hipError_t fwd_dispatch(bool w_f32, const FwdParams& p, int grid, hipStre
     return fwd_w<LPR, V, U, false, false>(w_f32, p, grid, s);
 }
 
-// `layout` indexes the residual table when p.r is set, else the plain one.
-hipError_t launch_fwd(int layout, bool w_f32, const FwdParams& p, int grid, hipStream_t s)
+hipError_t launch_fwd(int table, int layout, bool w_f32, const FwdParams& p, int grid, hipStream_t s)
 {
-    if (p.r) {
+    if ((table == FWD_RES) != (p.r != nullptr) || (table == FWD_LONG && p.g)) return hipErrorInvalidValue;
+    if (table == FWD_LONG) {
+        switch (layout) {
+#define RMSN_FWD_LONG_CASE(id, mh, l, vv, uu, kk) \
+    case id: return fwd_w<l, vv, uu, false, false>(w_f32, p, grid, s);
+            RMSN_FWD_LONG_LAYOUTS(RMSN_FWD_LONG_CASE)
+#undef RMSN_FWD_LONG_CASE
+        default: return hipErrorInvalidValue;
+        }
+    }
+    if (table == FWD_RES) {
         switch (layout) {
 #define RMSN_FWD_RES_CASE(id, mh, l, vv, uu, kk) \
     case id: return fwd_w<l, vv, uu, true, false>(w_f32, p, grid, s);

@@ -67,8 +67,10 @@ struct BwdParams {
 };
 
 // Launchers; return the launch's hipError_t.
-// launch_fwd: `layout` indexes kFwdResLayouts when p.r is set, else kFwdLayouts.
-hipError_t launch_fwd(int layout, bool w_f32, const FwdParams& p, int grid, hipStream_t s);
+// launch_fwd: `layout` indexes the forward table `table` (FWD_PLAIN, FWD_LONG
+// or FWD_RES of layouts.h; FWD_RES exactly when p.r is set, never FWD_LONG
+// with a gate).
+hipError_t launch_fwd(int table, int layout, bool w_f32, const FwdParams& p, int grid, hipStream_t s);
 hipError_t launch_bwd(int layout, bool w_f32, const BwdParams& p, hipStream_t s);
 hipError_t launch_dw_reduce(const double* part, int chunks, int H, float* dw, hipStream_t s);
 hipError_t launch_fill_zero(void* ptr, int64_t bytes, hipStream_t s);

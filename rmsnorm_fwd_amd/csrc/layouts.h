@@ -28,7 +28,8 @@ struct Layout {
 // X(id, max_h, lpr, v, u, k); max_h == lpr * v * 8.  Every entry was picked
 // by timing the candidates on MI355X with cold caches (T*H between 2^25 and
 // 2^30 elements); the smallest max_h >= H serves H.  A tuning build may
-// supply its own candidate tables (all three) through RMSN_LAYOUTS_OVERRIDE.
+// supply its own candidate tables (all four, and kFwdLongRows) through
+// RMSN_LAYOUTS_OVERRIDE.
 #ifdef RMSN_LAYOUTS_OVERRIDE
 #include RMSN_LAYOUTS_OVERRIDE
 #else
@@ -45,6 +46,29 @@ struct Layout {
     X(9, 5120, 320, 2, 2, 32)  \
     X(10, 6144, 768, 1, 2, 24) \
     X(11, 8192, 512, 2, 2, 32) \
+    X(12, 16384, 512, 4, 1, 8)
+
+// Plain forwards over at least kFwdLongRows rows.  Same lanes and vectors
+// per row as the plain table (so the same row sums); at H 4096 and 5120 three
+// rows per row group and iteration instead of two: T 65536, H 4096: 180 ->
+// 175 us; T 131072, H 4096: 364 -> 358 us; T 65536, H 5120: 228 -> 224 us.
+// Below that the extra rows cost more than they bring (T 16384, H 4096:
+// 47.4 -> 48.6 us; T 32768, H 5120: 110.9 -> 113.6 us), and at H 6144 and the
+// narrower widths they were slower at every row count measured.
+constexpr long long kFwdLongRows = 65536;
+#define RMSN_FWD_LONG_LAYOUTS(X) \
+    X(0, 64, 8, 1, 4, 64)        \
+    X(1, 128, 16, 1, 4, 64)      \
+    X(2, 256, 8, 4, 1, 64)       \
+    X(3, 512, 32, 2, 2, 64)      \
+    X(4, 1024, 32, 4, 1, 64)     \
+    X(5, 1536, 32, 6, 1, 16)     \
+    X(6, 2048, 256, 1, 4, 32)    \
+    X(7, 3072, 64, 6, 1, 32)     \
+    X(8, 4096, 512, 1, 3, 32)    \
+    X(9, 5120, 320, 2, 3, 32)    \
+    X(10, 6144, 768, 1, 2, 24)   \
+    X(11, 8192, 512, 2, 2, 32)   \
     X(12, 16384, 512, 4, 1, 8)
 
 // The forward with a fused residual add streams four tensors (x, r in; h, y
@@ -88,6 +112,7 @@ struct Layout {
 
 #define RMSN_CHECK_LAYOUT(id, mh, l, vv, uu, kk) static_assert((mh) == (l) * (vv) * 8, "layout width");
 RMSN_FWD_LAYOUTS(RMSN_CHECK_LAYOUT)
+RMSN_FWD_LONG_LAYOUTS(RMSN_CHECK_LAYOUT)
 RMSN_FWD_RES_LAYOUTS(RMSN_CHECK_LAYOUT)
 RMSN_BWD_LAYOUTS(RMSN_CHECK_LAYOUT)
 #undef RMSN_CHECK_LAYOUT
@@ -105,21 +130,37 @@ RMSN_BWD_LAYOUTS(RMSN_CHECK_LDS)
 
 #define RMSN_LAYOUT_ENTRY(id, mh, l, vv, uu, kk) Layout{mh, l, vv, uu, kk},
 static constexpr Layout kFwdLayouts[] = {RMSN_FWD_LAYOUTS(RMSN_LAYOUT_ENTRY)};
+static constexpr Layout kFwdLongLayouts[] = {RMSN_FWD_LONG_LAYOUTS(RMSN_LAYOUT_ENTRY)};
 static constexpr Layout kFwdResLayouts[] = {RMSN_FWD_RES_LAYOUTS(RMSN_LAYOUT_ENTRY)};
 static constexpr Layout kBwdLayouts[] = {RMSN_BWD_LAYOUTS(RMSN_LAYOUT_ENTRY)};
 #undef RMSN_LAYOUT_ENTRY
 
 static constexpr int kNumFwdLayouts = sizeof(kFwdLayouts) / sizeof(kFwdLayouts[0]);
 static_assert(sizeof(kFwdResLayouts) == sizeof(kFwdLayouts), "one residual layout per forward layout");
+static_assert(sizeof(kFwdLongLayouts) == sizeof(kFwdLayouts), "one long-run layout per forward layout");
 
-// Same widths, lanes and vectors per row in both forward tables.
-constexpr bool fwd_tables_agree(int i = 0)
+// Same widths, lanes and vectors per row in every forward table.
+constexpr bool fwd_tables_agree(const Layout* t, int i = 0)
 {
-    return i == kNumFwdLayouts ||
-           (kFwdResLayouts[i].max_h == kFwdLayouts[i].max_h && kFwdResLayouts[i].lpr == kFwdLayouts[i].lpr &&
-            kFwdResLayouts[i].v == kFwdLayouts[i].v && fwd_tables_agree(i + 1));
+    return i == kNumFwdLayouts || (t[i].max_h == kFwdLayouts[i].max_h && t[i].lpr == kFwdLayouts[i].lpr &&
+                                   t[i].v == kFwdLayouts[i].v && fwd_tables_agree(t, i + 1));
 }
-static_assert(fwd_tables_agree(), "the residual forward keeps the plain forward's row layout");
+static_assert(fwd_tables_agree(kFwdResLayouts), "the residual forward keeps the plain forward's row layout");
+static_assert(fwd_tables_agree(kFwdLongLayouts), "long runs keep the plain forward's row layout");
+
+// Which forward table serves a call: the residual one with a residual; the
+// long-run one for plain (ungated) forwards over at least kFwdLongRows rows;
+// else the plain one.
+enum { FWD_PLAIN = 0, FWD_LONG = 1, FWD_RES = 2 };
+inline int fwd_table_kind(long long R, bool residual, bool gated)
+{
+    if (residual) return FWD_RES;
+    return (!gated && R >= kFwdLongRows) ? FWD_LONG : FWD_PLAIN;
+}
+inline const Layout* fwd_table(int kind)
+{
+    return kind == FWD_RES ? kFwdResLayouts : (kind == FWD_LONG ? kFwdLongLayouts : kFwdLayouts);
+}
 static constexpr int kNumBwdLayouts = sizeof(kBwdLayouts) / sizeof(kBwdLayouts[0]);
 
 // Workgroup size: the largest multiple of LPR not above 256, or LPR itself

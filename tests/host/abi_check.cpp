@@ -28,15 +28,16 @@ struct Calls {
     int fwd = 0, bwd = 0, reduce = 0, fill = 0;
     FwdParams fp{};
     BwdParams bp{};
-    int grid = 0, layout = -1, reduce_chunks = 0, reduce_h = 0;
+    int grid = 0, layout = -1, fwd_table = -1, reduce_chunks = 0, reduce_h = 0;
     int64_t fill_bytes = 0;
     const void* fill_ptr = nullptr;
 };
 static Calls g;
 
-hipError_t launch_fwd(int layout, bool, const FwdParams& p, int grid, hipStream_t)
+hipError_t launch_fwd(int table, int layout, bool, const FwdParams& p, int grid, hipStream_t)
 {
     ++g.fwd;
+    g.fwd_table = table;
     g.fp = p;
     g.grid = grid;
     g.layout = layout;
@@ -242,7 +243,9 @@ static void check_forward_shape(int64_t T, int64_t heads, int64_t H, bool residu
                                (float*)P(3), T, heads, H, heads * H, H, 1e-6, 1, nullptr);
     CHECK(st == RMSN_OK, "forward status %d", st);
     if (T * heads == 0) return;
-    const Layout* table = residual ? kFwdResLayouts : kFwdLayouts;
+    const int kind = residual ? FWD_RES : (T * heads >= kFwdLongRows ? FWD_LONG : FWD_PLAIN);
+    CHECK(g.fwd_table == kind, "forward table %d for R=%lld", g.fwd_table, (long long)(T * heads));
+    const Layout* table = fwd_table(kind);
     const Layout& L = table[g.layout];
     CHECK(H <= L.max_h && (g.layout == 0 || H > table[g.layout - 1].max_h), "forward layout for H=%lld",
           (long long)H);
@@ -251,9 +254,23 @@ static void check_forward_shape(int64_t T, int64_t heads, int64_t H, bool residu
     CHECK((g.fp.r != nullptr) == residual && (g.fp.h != nullptr) == residual, "forward residual pointers");
 }
 
+// The gated forward always takes the plain table, whatever the row count.
+static void check_gated_forward_table()
+{
+    const int64_t Ts[] = {1, 65535, 65536, 131072};
+    for (int64_t T : Ts) {
+        reset();
+        const int st = rmsnorm_gated_fwd(P(0), P(4), P(1), RMSN_W_BF16, P(2), (float*)P(3), T, 1, 4096, 4096, 4096,
+                                         1e-6, 1, nullptr);
+        CHECK(st == RMSN_OK && g.fwd == 1 && g.fwd_table == FWD_PLAIN && g.fp.g != nullptr,
+              "gated forward table for T=%lld", (long long)T);
+    }
+}
+
 int main()
 {
     check_error_paths();
+    check_gated_forward_table();
     const int64_t Ts[] = {1, 2, 3, 4, 5, 7, 16, 63, 64, 65, 255, 256, 257, 1000, 1024, 4096, 4099,
                           16384, 65536, 131072, 1 << 20, (int64_t(1) << 30) - 1};
     for (int64_t H = 8; H <= RMSN_MAX_H; H += (H < 1024 ? 8 : (H < 8192 ? 72 : 520))) {

@@ -30,12 +30,44 @@ def test_widths(H, wdt):
     print(H, wdt, rep)
 
 
-@pytest.mark.parametrize("H", [256, 1536, 4096, 6144])
+@pytest.mark.parametrize("H", [256, 1536, 4096, 5120, 6144])
 @pytest.mark.parametrize("wdt", ["bf16", "f32"])
 @pytest.mark.parametrize("dres", [False, True])
 def test_residual(H, wdt, dres):
     rep = run_case(Layout.plain(257, H), wdt, res=True, dres=dres, seed=7)
     print(H, wdt, dres, rep)
+
+
+@pytest.mark.parametrize("H", [1536, 4096, 5120, 6144])
+def test_forward_tables_give_the_same_rows(H):
+    # The plain forward takes another table from 65536 rows on, and the
+    # residual forward a third; all keep the row layout, so every row's y and
+    # rstd are the same bits whichever table ran: a long run (with a ragged
+    # tail) against shorter plain runs over the same rows, and the residual
+    # forward against the plain forward over its h.
+    import torch
+    import rmsnorm_fwd_amd as rn
+    from tests.helpers import EPS
+    g = torch.Generator(device="cuda").manual_seed(H)
+    R = 65536 + 37
+    x = torch.randn(R, H, generator=g, device="cuda").bfloat16()
+    r = torch.randn(R, H, generator=g, device="cuda").bfloat16()
+    for wdt in (torch.bfloat16, torch.float32):
+        w = (1 + 0.1 * torch.randn(H, generator=g, device="cuda")).to(wdt)
+        y, rstd, _ = rn.rmsnorm_fwd(x, w, EPS)
+        y0, rstd0, _ = rn.rmsnorm_fwd(x[:65535], w, EPS)
+        y1, rstd1, _ = rn.rmsnorm_fwd(x[-100:], w, EPS)
+        assert torch.equal(y[:65535], y0) and torch.equal(rstd[:65535], rstd0), "long run, head rows"
+        assert torch.equal(y[-100:], y1) and torch.equal(rstd[-100:], rstd1), "long run, tail rows"
+        del y0, y1
+        for n in (R, 257):
+            yr, rstdr, h = rn.rmsnorm_fwd(x[:n], w, EPS, residual=r[:n])
+            assert torch.equal(h, (x[:n].float() + r[:n].float()).bfloat16()), "residual output"
+            yp, rstdp, _ = rn.rmsnorm_fwd(h, w, EPS)
+            assert torch.equal(yr, yp) and torch.equal(rstdr, rstdp), f"residual forward, {n} rows"
+            del yr, h, yp
+        del y
+    torch.cuda.synchronize()
 
 
 @pytest.mark.parametrize("T", [1, 2, 3, 5, 17, 63, 64, 65, 127, 1000])
