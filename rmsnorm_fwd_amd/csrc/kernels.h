@@ -68,8 +68,8 @@ struct BwdParams {
 
 // Launchers; return the launch's hipError_t.
 // launch_fwd: `layout` indexes the forward table `table` (FWD_PLAIN, FWD_LONG
-// or FWD_RES of layouts.h; FWD_RES exactly when p.r is set, never FWD_LONG
-// with a gate).
+// or FWD_RES_LONG of layouts.h; FWD_LONG only without residual and gate,
+// FWD_RES_LONG only with a residual).
 hipError_t launch_fwd(int table, int layout, bool w_f32, const FwdParams& p, int grid, hipStream_t s);
 hipError_t launch_bwd(int layout, bool w_f32, const BwdParams& p, hipStream_t s);
 hipError_t launch_dw_reduce(const double* part, int chunks, int H, float* dw, hipStream_t s);

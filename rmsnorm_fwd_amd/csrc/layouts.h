@@ -28,7 +28,7 @@ struct Layout {
 // X(id, max_h, lpr, v, u, k); max_h == lpr * v * 8.  Every entry was picked
 // by timing the candidates on MI355X with cold caches (T*H between 2^25 and
 // 2^30 elements); the smallest max_h >= H serves H.  A tuning build may
-// supply its own candidate tables (all four, and kFwdLongRows) through
+// supply its own candidate tables (all four, and the two row thresholds) through
 // RMSN_LAYOUTS_OVERRIDE.
 #ifdef RMSN_LAYOUTS_OVERRIDE
 #include RMSN_LAYOUTS_OVERRIDE
@@ -72,15 +72,20 @@ constexpr long long kFwdLongRows = 65536;
     X(12, 16384, 512, 4, 1, 8)
 
 // The forward with a fused residual add streams four tensors (x, r in; h, y
-// out) instead of two.  It keeps the plain forward's lanes and vectors per
-// row for every width -- so its row sums, rstd and y are the plain forward's
-// bits for the same input h -- and differs only in rows per iteration and
-// grid cap where that was faster: at H 5120 and 6144 four rows per row group
-// and iteration keep twice the loads in flight (T 131072, H 6144: 1183 ->
-// 1104 us; T 65536, H 5120: 497 -> 475 us; the grid cap made no difference
-// between 8 and 32 workgroups per compute unit).  At H 4096 four rows were
-// slower (372 -> 386 us), so the plain layout stays there and below.
-#define RMSN_FWD_RES_LAYOUTS(X) \
+// out) instead of two.  Over at least kFwdResLongRows rows it keeps the plain
+// forward's lanes and vectors per row for every width -- so its row sums,
+// rstd and y are the plain forward's bits for the same input h -- and at
+// H 5120 and 6144 takes four rows per row group and iteration, twice the
+// loads in flight: T 131072, H 6144: 1183 -> 1104 us; T 65536, H 6144:
+// 572 -> 543 us; T 32768, H 6144: 279 -> 271 us; T 65536, H 5120: 497 ->
+// 475 us (the grid cap made no difference between 8 and 32 workgroups per
+// compute unit).  Below that it takes the plain table: at T 16384 four rows
+// were already 1 % slower, at T 4096 6 %, and at T 1 the 768-lane
+// workgroup's three unused rows cost 1.2 us.  At H 4096 four rows were
+// slower at T 65536 (372 -> 386 us), so the plain layout stays there and
+// below.
+constexpr long long kFwdResLongRows = 32768;
+#define RMSN_FWD_RES_LONG_LAYOUTS(X) \
     X(0, 64, 8, 1, 4, 64)       \
     X(1, 128, 16, 1, 4, 64)     \
     X(2, 256, 8, 4, 1, 64)      \
@@ -113,7 +118,7 @@ constexpr long long kFwdLongRows = 65536;
 #define RMSN_CHECK_LAYOUT(id, mh, l, vv, uu, kk) static_assert((mh) == (l) * (vv) * 8, "layout width");
 RMSN_FWD_LAYOUTS(RMSN_CHECK_LAYOUT)
 RMSN_FWD_LONG_LAYOUTS(RMSN_CHECK_LAYOUT)
-RMSN_FWD_RES_LAYOUTS(RMSN_CHECK_LAYOUT)
+RMSN_FWD_RES_LONG_LAYOUTS(RMSN_CHECK_LAYOUT)
 RMSN_BWD_LAYOUTS(RMSN_CHECK_LAYOUT)
 #undef RMSN_CHECK_LAYOUT
 
@@ -131,12 +136,12 @@ RMSN_BWD_LAYOUTS(RMSN_CHECK_LDS)
 #define RMSN_LAYOUT_ENTRY(id, mh, l, vv, uu, kk) Layout{mh, l, vv, uu, kk},
 static constexpr Layout kFwdLayouts[] = {RMSN_FWD_LAYOUTS(RMSN_LAYOUT_ENTRY)};
 static constexpr Layout kFwdLongLayouts[] = {RMSN_FWD_LONG_LAYOUTS(RMSN_LAYOUT_ENTRY)};
-static constexpr Layout kFwdResLayouts[] = {RMSN_FWD_RES_LAYOUTS(RMSN_LAYOUT_ENTRY)};
+static constexpr Layout kFwdResLongLayouts[] = {RMSN_FWD_RES_LONG_LAYOUTS(RMSN_LAYOUT_ENTRY)};
 static constexpr Layout kBwdLayouts[] = {RMSN_BWD_LAYOUTS(RMSN_LAYOUT_ENTRY)};
 #undef RMSN_LAYOUT_ENTRY
 
 static constexpr int kNumFwdLayouts = sizeof(kFwdLayouts) / sizeof(kFwdLayouts[0]);
-static_assert(sizeof(kFwdResLayouts) == sizeof(kFwdLayouts), "one residual layout per forward layout");
+static_assert(sizeof(kFwdResLongLayouts) == sizeof(kFwdLayouts), "one residual layout per forward layout");
 static_assert(sizeof(kFwdLongLayouts) == sizeof(kFwdLayouts), "one long-run layout per forward layout");
 
 // Same widths, lanes and vectors per row in every forward table.
@@ -145,21 +150,22 @@ constexpr bool fwd_tables_agree(const Layout* t, int i = 0)
     return i == kNumFwdLayouts || (t[i].max_h == kFwdLayouts[i].max_h && t[i].lpr == kFwdLayouts[i].lpr &&
                                    t[i].v == kFwdLayouts[i].v && fwd_tables_agree(t, i + 1));
 }
-static_assert(fwd_tables_agree(kFwdResLayouts), "the residual forward keeps the plain forward's row layout");
+static_assert(fwd_tables_agree(kFwdResLongLayouts), "the residual forward keeps the plain forward's row layout");
 static_assert(fwd_tables_agree(kFwdLongLayouts), "long runs keep the plain forward's row layout");
 
-// Which forward table serves a call: the residual one with a residual; the
-// long-run one for plain (ungated) forwards over at least kFwdLongRows rows;
-// else the plain one.
-enum { FWD_PLAIN = 0, FWD_LONG = 1, FWD_RES = 2 };
+// Which forward table serves a call: the long-run tables for plain
+// (ungated) forwards over at least kFwdLongRows rows and residual forwards
+// over at least kFwdResLongRows rows; else the plain table, which serves the
+// plain, gated and residual kernels alike.
+enum { FWD_PLAIN = 0, FWD_LONG = 1, FWD_RES_LONG = 2 };
 inline int fwd_table_kind(long long R, bool residual, bool gated)
 {
-    if (residual) return FWD_RES;
+    if (residual) return R >= kFwdResLongRows ? FWD_RES_LONG : FWD_PLAIN;
     return (!gated && R >= kFwdLongRows) ? FWD_LONG : FWD_PLAIN;
 }
 inline const Layout* fwd_table(int kind)
 {
-    return kind == FWD_RES ? kFwdResLayouts : (kind == FWD_LONG ? kFwdLongLayouts : kFwdLayouts);
+    return kind == FWD_RES_LONG ? kFwdResLongLayouts : (kind == FWD_LONG ? kFwdLongLayouts : kFwdLayouts);
 }
 static constexpr int kNumBwdLayouts = sizeof(kBwdLayouts) / sizeof(kBwdLayouts[0]);
 

@@ -243,7 +243,9 @@ static void check_forward_shape(int64_t T, int64_t heads, int64_t H, bool residu
                                (float*)P(3), T, heads, H, heads * H, H, 1e-6, 1, nullptr);
     CHECK(st == RMSN_OK, "forward status %d", st);
     if (T * heads == 0) return;
-    const int kind = residual ? FWD_RES : (T * heads >= kFwdLongRows ? FWD_LONG : FWD_PLAIN);
+    const int64_t R = T * heads;
+    const int kind = residual ? (R >= kFwdResLongRows ? FWD_RES_LONG : FWD_PLAIN)
+                              : (R >= kFwdLongRows ? FWD_LONG : FWD_PLAIN);
     CHECK(g.fwd_table == kind, "forward table %d for R=%lld", g.fwd_table, (long long)(T * heads));
     const Layout* table = fwd_table(kind);
     const Layout& L = table[g.layout];
@@ -257,7 +259,7 @@ static void check_forward_shape(int64_t T, int64_t heads, int64_t H, bool residu
 // The gated forward always takes the plain table, whatever the row count.
 static void check_gated_forward_table()
 {
-    const int64_t Ts[] = {1, 65535, 65536, 131072};
+    const int64_t Ts[] = {1, 32768, 65535, 65536, 131072};
     for (int64_t T : Ts) {
         reset();
         const int st = rmsnorm_gated_fwd(P(0), P(4), P(1), RMSN_W_BF16, P(2), (float*)P(3), T, 1, 4096, 4096, 4096,
@@ -272,7 +274,7 @@ int main()
     check_error_paths();
     check_gated_forward_table();
     const int64_t Ts[] = {1, 2, 3, 4, 5, 7, 16, 63, 64, 65, 255, 256, 257, 1000, 1024, 4096, 4099,
-                          16384, 65536, 131072, 1 << 20, (int64_t(1) << 30) - 1};
+                          16384, 32767, 32768, 65535, 65536, 131072, 1 << 20, (int64_t(1) << 30) - 1};
     for (int64_t H = 8; H <= RMSN_MAX_H; H += (H < 1024 ? 8 : (H < 8192 ? 72 : 520))) {
         for (int64_t T : Ts) {
             check_backward_shape(T, 1, H);

@@ -41,10 +41,11 @@ def test_residual(H, wdt, dres):
 @pytest.mark.parametrize("H", [1536, 4096, 5120, 6144])
 def test_forward_tables_give_the_same_rows(H):
     # The plain forward takes another table from 65536 rows on, and the
-    # residual forward a third; all keep the row layout, so every row's y and
-    # rstd are the same bits whichever table ran: a long run (with a ragged
-    # tail) against shorter plain runs over the same rows, and the residual
-    # forward against the plain forward over its h.
+    # residual forward another from 32768 rows on; all keep the row layout, so
+    # every row's y and rstd are the same bits whichever table ran: a long run
+    # (with a ragged tail) against shorter plain runs over the same rows, and
+    # the residual forward, long and short, against the plain forward over
+    # its h.
     import torch
     import rmsnorm_fwd_amd as rn
     from tests.helpers import EPS
@@ -60,7 +61,7 @@ def test_forward_tables_give_the_same_rows(H):
         assert torch.equal(y[:65535], y0) and torch.equal(rstd[:65535], rstd0), "long run, head rows"
         assert torch.equal(y[-100:], y1) and torch.equal(rstd[-100:], rstd1), "long run, tail rows"
         del y0, y1
-        for n in (R, 257):
+        for n in (R, 32768, 32767, 257):
             yr, rstdr, h = rn.rmsnorm_fwd(x[:n], w, EPS, residual=r[:n])
             assert torch.equal(h, (x[:n].float() + r[:n].float()).bfloat16()), "residual output"
             yp, rstdp, _ = rn.rmsnorm_fwd(h, w, EPS)
