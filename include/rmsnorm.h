@@ -83,6 +83,10 @@ enum rmsn_dtype { RMSN_W_BF16 = 0, RMSN_W_F32 = 1 };
  *   deterministic accepted for symmetry with the backward; the forward is
  *                the same program, bit for bit, in both modes (p1 #8577
  *                opening paragraph: both modes share one forward).
+ * A row's rstd and y (and h) depend only on that row, w, eps and H: the
+ * order of its sum of squares is fixed by H, whatever the row count, the
+ * strides or the residual (the grid and the rows per workgroup, which do
+ * vary with the row count, never split a row differently).
  */
 int rmsnorm_fwd(const void* x, const void* residual, const void* w, int w_dtype,
                 void* y, void* residual_out, float* rstd,
