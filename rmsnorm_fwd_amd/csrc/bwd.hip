@@ -147,10 +147,23 @@ __global__ void __launch_bounds__(block_of(LPR)) bwd_kernel(BwdParams p)
 #pragma unroll
         for (int e = 0; e < 8; ++e) acc[v][e] = 0.0;
 
+    // Gated rows of one vector per lane load the workgroup's next rows while
+    // the current ones are reduced (a second register tile): their
+    // workgroups fill a compute unit alone, so no other wavefront covers the
+    // load latency, and the tile fits the registers that occupancy leaves.
+    constexpr bool PF = GATE && V == 1;
     BwdTile<U, V, DRES, GATE> cur;
+    BwdTile<PF ? U : 1, PF ? V : 1, DRES, GATE> nxt;
+    if constexpr (PF) {
+        if (first < row1) bwd_load<U, V, SLOTS, DRES, GATE>(cur, p, lv, first, slot, row1);
+    }
     int it = 0;
     for (int base = first; base < row1; base += step, ++it) {
-        bwd_load<U, V, SLOTS, DRES, GATE>(cur, p, lv, base, slot, row1);
+        if constexpr (PF) {
+            if (base + step < row1) bwd_load<U, V, SLOTS, DRES, GATE>(nxt, p, lv, base + step, slot, row1);
+        } else {
+            bwd_load<U, V, SLOTS, DRES, GATE>(cur, p, lv, base, slot, row1);
+        }
         const bool* ok = cur.ok;
         const int64_t* off = cur.off;
         const double* rho = cur.rho;
@@ -218,6 +231,9 @@ __global__ void __launch_bounds__(block_of(LPR)) bwd_kernel(BwdParams p)
                 o.w = pack_bf16x2_from_f64(d[6], d[7]);
                 if (ok[u] && lv.ok[v]) st16_stream(p.dx + off[u] + lv.col[v], o);
             }
+        }
+        if constexpr (PF) {
+            if (base + step < row1) cur = nxt;
         }
     }
 
@@ -353,7 +369,10 @@ constexpr int gated_u() { return LPR <= 256 ? 1 : U; }
 #endif
 // Gated rows of three vectors per lane spill even at one row per row group;
 // they run as rows of three times the lanes and one vector each instead
-// (the gated variant's row order is then its own, fixed per H).
+// (the gated variant's row order is then its own, fixed per H), which also
+// gives them the double-buffered loads of one-vector gated rows.  Rows of
+// two vectors stay as they are: as rows of twice the lanes they ran 1.2-1.4x
+// slower, and the second tile does not fit their registers.
 template <int LPR, int V, int U>
 static hipError_t bwd_gated(bool w_f32, const BwdParams& p, hipStream_t s)
 {

@@ -138,6 +138,14 @@ def test_gated_head_view():
     print(run_gated(Layout.heads_view(512, 24, 256, 8192, 256), "bf16", seed=3))
 
 
+@pytest.mark.parametrize("T,H", [(4099, 1536), (4099, 3072), (4099, 5120), (4099, 6144), (40000, 64)])
+def test_gated_rows_over_several_iterations(T, H):
+    # one-vector gated rows load a workgroup's next rows while reducing the
+    # current ones; these row counts give every workgroup several iterations
+    # and a ragged last one
+    print(T, H, run_gated(Layout.plain(T, H), "bf16", seed=T + H))
+
+
 def test_gated_large():
     print(run_gated(Layout.plain(16384, 4096), "f32", seed=5, det_repeats=3))
 
