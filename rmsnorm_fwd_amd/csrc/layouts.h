@@ -9,9 +9,11 @@
 // DPP and ds_swizzle only); LPR > 64 spans LPR/64 wavefronts that combine
 // their partial sums through LDS.  A workgroup has BLOCK = max(256, LPR)
 // lanes, i.e. SLOTS = BLOCK/LPR row groups, and each row group takes U rows
-// per iteration, so one iteration covers RPI = SLOTS*U rows.  The layout is
-// a function of H alone, which keeps the order of every row reduction --
-// and so y, rstd and dx -- independent of T, of the route and of the mode.
+// per iteration, so one iteration covers RPI = SLOTS*U rows.  LPR and V are
+// a function of H alone (the forward's U and grid cap also follow the row
+// count and the residual, through the tables below, which all agree on LPR
+// and V), which keeps the order of every row reduction -- and so y, rstd
+// and dx -- independent of T, of the route and of the mode.
 #pragma once
 
 namespace rmsn {
