@@ -567,7 +567,11 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16 storage; fp32/fp64 accumulation",
+        # the arithmetic the kernels compute in: FP32 products, FP64 row and
+        # column sums; activations are stored as BF16
+        "dtype": "f32",
+        "storage_dtype": "bf16",
+        "accumulation": "f64 row sums and dw column sums",
         "data": "synthetic (seeded N(0,1) x and dy, w = 1 + 0.1 N(0,1))",
         "config": {"workload": wl.name, "T": wl.T, "heads": wl.heads, "H": wl.H, "w_dtype": wl.wdt,
                    "residual": wl.res, "silu_gate": wl.gate,
