@@ -71,6 +71,44 @@ def test_forward_tables_give_the_same_rows(H):
     torch.cuda.synchronize()
 
 
+@pytest.mark.parametrize("heads,H,res", [(4, 4096, False), (5, 5120, False), (4, 6144, True), (3, 5120, True)])
+def test_forward_tables_on_head_views(heads, H, res):
+    # strided [T, heads, H] views whose row count T*heads crosses into the
+    # long-run tables: every row's y, rstd (and h) must be the bits the same
+    # rows give as a contiguous [T*heads, H] run of the short-run table
+    import torch
+    import rmsnorm_fwd_amd as rn
+    from tests.helpers import EPS
+    R_min = 32768 if res else 65536
+    T = -(-R_min // heads) + 7
+    g = torch.Generator(device="cuda").manual_seed(H + heads)
+    pad = 24
+    xb = torch.randn(T, heads, H + pad, generator=g, device="cuda").bfloat16()
+    rb = torch.randn(T, heads, H + pad, generator=g, device="cuda").bfloat16() if res else None
+    x = xb[..., :H]
+    r = rb[..., :H] if res else None
+    w = (1 + 0.1 * torch.randn(H, generator=g, device="cuda")).bfloat16()
+    sentinel = torch.tensor(-12345.0, dtype=torch.bfloat16, device="cuda")
+    yb = sentinel.expand(T, heads, H + pad).clone()
+    hb = sentinel.expand(T, heads, H + pad).clone() if res else None
+    y, rstd, h = rn.rmsnorm_fwd(x, w, EPS, residual=r, y=yb[..., :H], residual_out=hb[..., :H] if res else None)
+    assert T * heads >= R_min
+    xc = x.reshape(T * heads, H).contiguous()
+    rc = r.reshape(T * heads, H).contiguous() if res else None
+    half = (T * heads) // 2  # two short runs, each below the threshold
+    for lo, hi in ((0, half), (half, T * heads)):
+        yc, rstdc, hc = rn.rmsnorm_fwd(xc[lo:hi], w, EPS, residual=rc[lo:hi] if res else None)
+        assert torch.equal(y.reshape(T * heads, H)[lo:hi], yc), (lo, hi, "y")
+        assert torch.equal(rstd[lo:hi], rstdc), (lo, hi, "rstd")
+        if res:
+            assert torch.equal(h.reshape(T * heads, H)[lo:hi], hc), (lo, hi, "h")
+    # the padding between heads is left alone
+    assert bool((yb[..., H:] == sentinel).all()), "y padding written"
+    if res:
+        assert bool((hb[..., H:] == sentinel).all()), "h padding written"
+    torch.cuda.synchronize()
+
+
 @pytest.mark.parametrize("T", [1, 2, 3, 5, 17, 63, 64, 65, 127, 1000])
 def test_row_counts(T):
     run_case(Layout.plain(T, 2048), "bf16", seed=T)
