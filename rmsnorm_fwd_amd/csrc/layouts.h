@@ -29,7 +29,11 @@ struct Layout {
 
 // X(id, max_h, lpr, v, u, k); max_h == lpr * v * 8.  Every entry was picked
 // by timing the candidates on MI355X with cold caches (T*H between 2^25 and
-// 2^30 elements); the smallest max_h >= H serves H.  A tuning build may
+// 2^30 elements); the smallest max_h >= H serves H.  At H 4096 and 5120 the
+// forward's grid cap is 64 workgroups per compute unit (one or two
+// iterations each): against 32, 1-3 % faster from T 32768 up (T 131072,
+// H 4096: 358 -> 348 us; gated T 65536, H 4096: 269 -> 262 us) and equal
+// below; at H 6144 64 was 2 % slower at T 16384.  A tuning build may
 // supply its own candidate tables (all four, and the two row thresholds) through
 // RMSN_LAYOUTS_OVERRIDE.
 #ifdef RMSN_LAYOUTS_OVERRIDE
@@ -44,8 +48,8 @@ struct Layout {
     X(5, 1536, 32, 6, 1, 16)   \
     X(6, 2048, 256, 1, 4, 32)  \
     X(7, 3072, 64, 6, 1, 32)   \
-    X(8, 4096, 512, 1, 2, 32)  \
-    X(9, 5120, 320, 2, 2, 32)  \
+    X(8, 4096, 512, 1, 2, 64)  \
+    X(9, 5120, 320, 2, 2, 64)  \
     X(10, 6144, 768, 1, 2, 24) \
     X(11, 8192, 512, 2, 2, 32) \
     X(12, 16384, 512, 4, 1, 8)
@@ -67,8 +71,8 @@ constexpr long long kFwdLongRows = 65536;
     X(5, 1536, 32, 6, 1, 16)     \
     X(6, 2048, 256, 1, 4, 32)    \
     X(7, 3072, 64, 6, 1, 32)     \
-    X(8, 4096, 512, 1, 3, 32)    \
-    X(9, 5120, 320, 2, 3, 32)    \
+    X(8, 4096, 512, 1, 3, 64)    \
+    X(9, 5120, 320, 2, 3, 64)    \
     X(10, 6144, 768, 1, 2, 24)   \
     X(11, 8192, 512, 2, 2, 32)   \
     X(12, 16384, 512, 4, 1, 8)
