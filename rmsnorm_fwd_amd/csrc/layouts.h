@@ -29,11 +29,14 @@ struct Layout {
 
 // X(id, max_h, lpr, v, u, k); max_h == lpr * v * 8.  Every entry was picked
 // by timing the candidates on MI355X with cold caches (T*H between 2^25 and
-// 2^30 elements); the smallest max_h >= H serves H.  At H 4096 and 5120 the
-// forward's grid cap is 64 workgroups per compute unit (one or two
+// 2^30 elements); the smallest max_h >= H serves H.  At H 2048, 4096 and
+// 5120 the forward's grid cap is 64 workgroups per compute unit (one or two
 // iterations each): against 32, 1-3 % faster from T 32768 up (T 131072,
-// H 4096: 358 -> 348 us; gated T 65536, H 4096: 269 -> 262 us) and equal
-// below; at H 6144 64 was 2 % slower at T 16384.  A tuning build may
+// H 4096: 358 -> 348 us; gated T 65536, H 4096: 269 -> 262 us; T 65536,
+// H 2048: 91.3 -> 89.5 us) and equal below.  At H 6144 a larger cap pays
+// only in long runs (48: T 131072 548 -> 540 us), and was 2 % slower at
+// T 16384, so only the long-run table takes it; at H 1536 and 3072 it made
+// no difference.  A tuning build may
 // supply its own candidate tables (all four, and the two row thresholds) through
 // RMSN_LAYOUTS_OVERRIDE.
 #ifdef RMSN_LAYOUTS_OVERRIDE
@@ -46,7 +49,7 @@ struct Layout {
     X(3, 512, 32, 2, 2, 64)    \
     X(4, 1024, 32, 4, 1, 64)   \
     X(5, 1536, 32, 6, 1, 16)   \
-    X(6, 2048, 256, 1, 4, 32)  \
+    X(6, 2048, 256, 1, 4, 64)  \
     X(7, 3072, 64, 6, 1, 32)   \
     X(8, 4096, 512, 1, 2, 64)  \
     X(9, 5120, 320, 2, 2, 64)  \
@@ -69,11 +72,11 @@ constexpr long long kFwdLongRows = 65536;
     X(3, 512, 32, 2, 2, 64)      \
     X(4, 1024, 32, 4, 1, 64)     \
     X(5, 1536, 32, 6, 1, 16)     \
-    X(6, 2048, 256, 1, 4, 32)    \
+    X(6, 2048, 256, 1, 4, 64)    \
     X(7, 3072, 64, 6, 1, 32)     \
     X(8, 4096, 512, 1, 3, 64)    \
     X(9, 5120, 320, 2, 3, 64)    \
-    X(10, 6144, 768, 1, 2, 24)   \
+    X(10, 6144, 768, 1, 2, 48)   \
     X(11, 8192, 512, 2, 2, 32)   \
     X(12, 16384, 512, 4, 1, 8)
 
