@@ -508,8 +508,9 @@ def main():
         return
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py measures one GPU only: this build has no multi-GPU path "
-              "(dw would need one all-reduce of H values; see the design notes). Run with --gpus 1.",
+        print("bench.py measures one GPU only: the library has no multi-GPU path "
+              "(rows split across GPUs with no exchange; dw would need one all-reduce of H values). "
+              "Run with --gpus 1.",
               file=sys.stderr)
         sys.exit(2)
 
