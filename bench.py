@@ -1,18 +1,29 @@
 """Benchmark of the MI355X training RMSNorm on one GPU.
 
-Workload (default): T=65536 rows of H=4096 BF16 values, FP32 weight
-w = 1 + 0.1 N(0,1), x and dy ~ N(0,1), eps = 1e-6, plain rows -- the shape the
-pages' headline comparison is quoted on.  A step is the pages' checkpointed
-training step "2xfwd+bwd" (forward, forward recompute, backward; p2
-"Key": op 2xfwd+bwd), here with the deterministic backward.
+Workload (default): the largest of the measured workloads, T=131072 rows of
+H=6144 with the fused residual add -- x, r, dy ~ N(0,1) BF16, BF16 weight
+w = 1 + 0.1 N(0,1), eps = 1e-6; the forward reads x and r and writes h and
+y, the backward reads h and dy (dres = NULL, the workload names only dy).
+A step is the pages' checkpointed training step "2xfwd+bwd" (forward,
+forward recompute, backward; p2 "Key": op 2xfwd+bwd), here with the
+deterministic backward.
 
 Printed: ONE JSON line.  `value` is the step's effective HBM throughput
 (algorithmic bytes of fwd + fwd + bwd over the measured step time, back to
 back with inputs resident in HBM).  Beside it the line carries, per op and
 mode, latency with L2 and the 256 MB last-level cache flushed before every
 launch (the pages' protocol: cold L2, median of many launches), the
-per-kernel roofline of the dominant kernel from HIP events, and the CPU
-oracle timed on the host as a baseline.
+roofline of the dominant kernel (the forward) and of the backward from
+HIP events around every launch of a second run of K steps, the same
+figures for the T=65536 x H=4096 FP32-weight workload, and the CPU oracle
+timed on the host as a baseline.
+
+Roofline basis.  `roofline.achieved` = algorithmic bytes per launch / the
+mean duration of the kernel's launches, each launch bracketed by HIP events
+on the library's stream, over the warm-up steps and both runs of K steps.
+`rocprofv3 --kernel-trace --stats` of `bench.py --profile` (which runs
+exactly those steps and nothing else) averages the same launches;
+`--profile-report` writes that summary under profiles/ with both figures.
 
 Algorithmic bytes (what the operation must move; workspace traffic excluded):
   fwd = 4 R H (+4 R H with a residual) + 4 R + sw H
@@ -54,7 +65,8 @@ WORKLOADS = {
     "T65536_H4096_w32_gate": (65536, 1, 4096, 4096, 4096, "f32", "gate"),
     "T65536_H6144_gate": (65536, 1, 6144, 6144, 6144, "bf16", "gate"),
 }
-DEFAULT_WORKLOAD = "T65536_H4096_w32"
+DEFAULT_WORKLOAD = "T131072_H6144_res"
+EXTRA_WORKLOADS = ("T65536_H4096_w32",)
 
 
 def fwd_bytes(R, H, sw, res, gate=False):
@@ -120,7 +132,8 @@ class Workload:
         self.dx = self.view(place(self.x_h))
         self.rstd = torch.empty(self.R, dtype=torch.float32, device=dev)
         self.dw = torch.empty(H, dtype=torch.float32, device=dev)
-        self.ws = rn.rmsnorm_bwd_workspace(T, heads, H, dev)
+        self.ws = rn.rmsnorm_bwd_workspace(T, heads, H, dev, w_dtype=rn.RMSN_W_F32 if wdt == "f32" else rn.RMSN_W_BF16,
+                                           has_residual=res)
         self.fwd_bytes = fwd_bytes(self.R, H, self.sw, res, self.gate)
         self.bwd_bytes = bwd_bytes(self.R, H, self.sw, False, self.gate)
         self.step_bytes = 2 * self.fwd_bytes + self.bwd_bytes
@@ -242,7 +255,6 @@ def profiled_traffic(workload, kernel):
     """HBM bytes per launch of `kernel` from the committed rocprofv3 summary
     for this workload, or None if there is none or the kernel's sources have
     changed since it was taken."""
-    import hashlib
     import re
 
     path = os.path.join(ROOT, "profiles", f"rmsnorm_kernels_{workload}.md")
@@ -254,13 +266,7 @@ def profiled_traffic(workload, kernel):
     rec = json.loads(m.group(1)).get("kernels", {}).get(kernel)
     if not rec:
         return None
-    srcs = {"fwd_kernel": ["fwd.hip", "device_common.h", "kernels.h", "layouts.h"],
-            "bwd_kernel": ["bwd.hip", "device_common.h", "kernels.h", "layouts.h"]}[kernel]
-    h = hashlib.sha256()
-    for f in srcs:
-        with open(os.path.join(ROOT, "rmsnorm_fwd_amd", "csrc", f), "rb") as fh:
-            h.update(fh.read())
-    return rec["traffic_bytes"] if h.hexdigest()[:16] == rec["source_hash"] else None
+    return rec["traffic_bytes"] if source_hash(kernel) == rec["source_hash"] else None
 
 
 # The pages' latency tables (p1 #8577, per-shape fwd/bwd/step rows) cover
@@ -311,7 +317,8 @@ class DeviceCase:
         self.dx = torch.empty_like(self.x)
         self.rstd = torch.empty(T, dtype=torch.float32, device="cuda")
         self.dw = torch.empty(H, dtype=torch.float32, device="cuda")
-        self.ws = rn.rmsnorm_bwd_workspace(T, 1, H, "cuda")
+        self.ws = rn.rmsnorm_bwd_workspace(T, 1, H, "cuda", w_dtype=rn.RMSN_W_F32 if wdt == "f32" else rn.RMSN_W_BF16,
+                                           has_residual=res)
 
     def fwd(self):
         self.rn.rmsnorm_fwd(self.x, self.w, EPS, residual=self.r, y=self.y, residual_out=self.h,
@@ -478,26 +485,295 @@ def _rows_view(a, rows):
     return a[:rows] if a is not None else None
 
 
+class LaunchTimer:
+    """HIP events around every launch of the ops it wraps, on torch's current
+    stream (the stream the library's calls are enqueued on)."""
+
+    def __init__(self):
+        self.ev = {}
+
+    def __call__(self, name, fn):
+        import torch
+
+        a = torch.cuda.Event(enable_timing=True)
+        b = torch.cuda.Event(enable_timing=True)
+        a.record()
+        fn()
+        b.record()
+        self.ev.setdefault(name, []).append((a, b))
+
+    def us(self, name):
+        import torch
+
+        torch.cuda.synchronize()
+        return [a.elapsed_time(b) * 1e3 for a, b in self.ev.get(name, [])]
+
+
+def timed_step(wl, timer, det=True):
+    timer("fwd", wl.fwd)
+    timer("fwd", wl.fwd)
+    timer("bwd", lambda: wl.bwd(det))
+
+
+def roofline_of(wl, fwd_us, bwd_us, basis):
+    """The forward (two launches per step, the larger share of it) is the
+    dominant kernel; the backward (row kernel, plus the fixed-order reduce
+    where the route has one) beside it."""
+    f_mean, b_mean = statistics.fmean(fwd_us), statistics.fmean(bwd_us)
+    f_gbs = wl.fwd_bytes / (f_mean * 1e-6) / 1e9
+    b_gbs = wl.bwd_bytes / (b_mean * 1e-6) / 1e9
+    roof = {"bound": "hbm", "kernel": "fwd_kernel", "achieved": round(f_gbs, 1), "peak": PEAK_GBS,
+            "unit": "GB/s", "frac": round(f_gbs / PEAK_GBS, 4),
+            "traffic": profiled_traffic(wl.name, "fwd_kernel"), "basis": basis,
+            "us_per_launch_mean": round(f_mean, 2), "us_per_launch_median": round(statistics.median(fwd_us), 2),
+            "launches": len(fwd_us), "bytes_per_launch": wl.fwd_bytes}
+    roof_b = {"bound": "hbm", "kernel": "bwd_kernel (+ dw_reduce_kernel when routed), deterministic",
+              "achieved": round(b_gbs, 1), "peak": PEAK_GBS, "unit": "GB/s", "frac": round(b_gbs / PEAK_GBS, 4),
+              "traffic_row_kernel": profiled_traffic(wl.name, "bwd_kernel"), "basis": basis,
+              "us_per_call_mean": round(b_mean, 2), "us_per_call_median": round(statistics.median(bwd_us), 2),
+              "calls": len(bwd_us), "bytes_per_call": wl.bwd_bytes}
+    return roof, roof_b
+
+
+def measure_workload(wl, args):
+    """Warm-up, K timed steps (whole-step events), K more steps with every
+    launch bracketed (roofline); returns the step time and the per-launch
+    lists of the bracketed run.  With --profile nothing else runs, so a
+    profiler sees exactly these launches."""
+    import torch
+
+    for _ in range(args.warmup):
+        wl.step(True)
+    torch.cuda.synchronize()
+    log(f"{wl.name}: warmup {args.warmup} steps done")
+    ev0 = torch.cuda.Event(enable_timing=True)
+    ev1 = torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    ev0.record()
+    for _ in range(args.steps):
+        wl.step(True)
+    ev1.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_per_step = ev0.elapsed_time(ev1) / args.steps
+    timer = LaunchTimer()
+    for _ in range(args.steps):
+        timed_step(wl, timer)
+    fwd_us, bwd_us = timer.us("fwd"), timer.us("bwd")
+    log(f"{wl.name}: timed {args.steps} steps: {ms_per_step * 1e3:.1f} us/step (wall {wall:.3f}s); "
+        f"per launch fwd {statistics.fmean(fwd_us):.1f} us, bwd {statistics.fmean(bwd_us):.1f} us")
+    return ms_per_step, fwd_us, bwd_us
+
+
+def cold_latencies(wl, args, flush):
+    """Per-op latency with cold caches; "fwd_aa" is the forward again, timed
+    as if it were another implementation (the A/A floor of the method)."""
+    ops = {
+        "fwd": (wl.fwd, wl.fwd_bytes),
+        "fwd_aa": (wl.fwd, wl.fwd_bytes),
+        "bwd_det": (lambda: wl.bwd(True), wl.bwd_bytes),
+        "bwd_nondet": (lambda: wl.bwd(False), wl.bwd_bytes),
+        **({"bwd_det_dres": (lambda: wl.bwd(True, wl.dres), bwd_bytes(wl.R, wl.H, wl.sw, True))}
+           if wl.res else {}),
+        "step_det": (lambda: wl.step(True), wl.step_bytes),
+        "step_nondet": (lambda: wl.step(False), wl.step_bytes),
+    }
+    ops["step_det_graph"] = (graphed(lambda: wl.step(True)), wl.step_bytes)
+    for fn, _ in ops.values():
+        for _ in range(3):
+            fn()
+    reps = max(1, -(-args.cold_reps // args.cold_rounds))
+    raw = time_cold({k: v[0] for k, v in ops.items()}, args.cold_rounds, reps, flush)
+    lat = {}
+    for name, (_, nbytes) in ops.items():
+        c = summarize(raw[name])
+        c["gbs"] = round(nbytes / (c["median_us"] * 1e-6) / 1e9, 1)
+        c["pct_peak"] = round(100 * c["gbs"] / PEAK_GBS, 2)
+        c["bytes"] = nbytes
+        lat[name] = c
+        log(f"{wl.name}: cold {name}: {c['median_us']:.1f} us  {c['gbs']:.0f} GB/s ({c['pct_peak']:.1f}%)")
+    lat["aa_floor_pct"] = round(100 * abs(lat["fwd"]["median_us"] - lat["fwd_aa"]["median_us"])
+                                / lat["fwd"]["median_us"], 3)
+    # deterministic over non-deterministic backward time (> 1: non-det faster)
+    lat["mode_ratio_bwd"] = round(lat["bwd_det"]["median_us"] / lat["bwd_nondet"]["median_us"], 4)
+    return lat
+
+
+def route_of(wl, rn):
+    route = {}
+    names = {0: "pair", 1: "atomic", 2: "cols", 3: "cols_ticket"}
+    for det in (1, 0):
+        f, chunks, cc, cv = rn.rmsnorm_bwd_route(wl.T, wl.heads, wl.H, 1 if wl.wdt == "f32" else 0, wl.res, det)
+        route["det" if det else "nondet"] = {"form": names.get(f, f), "chunks": chunks, "col_chunks": cc,
+                                             "col_vecs": cv}
+    return route
+
+
+# ---- rocprofv3 summaries (profiles/rmsnorm_kernels_<workload>.md) --------
+
+PROFILE_KERNELS = ("fwd_kernel", "bwd_kernel", "bwd_cols_kernel", "dw_reduce_kernel")
+PROFILE_SOURCES = {"fwd_kernel": ["fwd.hip", "device_common.h", "kernels.h", "layouts.h"],
+                   "bwd_kernel": ["bwd.hip", "device_common.h", "kernels.h", "layouts.h"],
+                   "bwd_cols_kernel": ["bwd.hip", "device_common.h", "kernels.h", "layouts.h"],
+                   "dw_reduce_kernel": ["bwd.hip", "device_common.h", "kernels.h", "layouts.h"]}
+
+
+def source_hash(kernel):
+    import hashlib
+
+    h = hashlib.sha256()
+    for f in PROFILE_SOURCES[kernel]:
+        with open(os.path.join(ROOT, "rmsnorm_fwd_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def profile_commands(workload, steps, warmup):
+    base = f"python3 R/bench.py --profile --steps {steps} --warmup {warmup} --workload {workload} --copy-calibration"
+    return [f"rocprofv3 --kernel-trace --stats --output-format csv -d OUT/ktrace -o run -- {base} > OUT/ktrace.log",
+            f"rocprofv3 --pmc FETCH_SIZE --output-format csv -d OUT/fetch -o run -- {base}",
+            f"rocprofv3 --pmc WRITE_SIZE --output-format csv -d OUT/write -o run -- {base}",
+            f"python3 R/bench.py --profile-report OUT {workload} {steps} {warmup}"]
+
+
+def profile_report(out_dir, workload, steps, warmup):
+    """The markdown summary of three rocprofv3 runs of `bench.py --profile`
+    (a kernel trace with --stats, then FETCH_SIZE, then WRITE_SIZE): kernel
+    statistics, HBM bytes per dispatch scaled by a plain 1 GiB device copy
+    in the same process, and the bench's own event-based roofline from the
+    trace run's JSON line beside the trace's averages."""
+    import csv
+    import glob
+
+    def one(pattern):
+        hits = sorted(glob.glob(os.path.join(out_dir, pattern), recursive=True))
+        if not hits:
+            raise SystemExit(f"no {pattern} under {out_dir}")
+        return hits[0]
+
+    def key_of(name):
+        for k in PROFILE_KERNELS:
+            if f"rmsn::{k}" in name:
+                return k
+        return None
+
+    stats = list(csv.DictReader(open(one("ktrace/**/*kernel_stats.csv"))))
+    trace = list(csv.DictReader(open(one("ktrace/**/*kernel_trace.csv"))))
+    trace.sort(key=lambda r: int(r["Dispatch_Id"]))
+    durs = {}
+    for r in trace:
+        k = key_of(r["Kernel_Name"])
+        if k:
+            durs.setdefault(k, []).append((int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3)
+    # bench.py --profile runs W warm-up steps, K timed steps, then K steps
+    # with every launch bracketed: two forwards and one backward per step
+    per_step = {"fwd_kernel": 2, "bwd_kernel": 1, "bwd_cols_kernel": 1, "dw_reduce_kernel": 1}
+    last_run = {k: v[-per_step[k] * steps:] for k, v in durs.items() if len(v) >= per_step[k] * (warmup + 2 * steps)}
+
+    def counters(kind):
+        rows = list(csv.DictReader(open(one(f"{kind}/**/*counter_collection.csv"))))
+        rows.sort(key=lambda r: int(r["Dispatch_Id"]))
+        copies = [float(r["Counter_Value"]) for r in rows if r["Kernel_Name"].startswith("__amd_rocclr_copyBuffer")]
+        per = {}
+        for r in rows:
+            per.setdefault(r["Kernel_Name"], []).append(float(r["Counter_Value"]))
+        return copies[:3], {k: sum(v) / len(v) for k, v in per.items()}
+
+    fc, fetch = counters("fetch")
+    wc, write = counters("write")
+    gib_kib = 1048576.0
+    fscale = gib_kib / (sum(fc) / len(fc))
+    wscale = gib_kib / (sum(wc) / len(wc))
+    bench_line = None
+    for path in glob.glob(os.path.join(out_dir, "ktrace*.log")) + glob.glob(os.path.join(out_dir, "*.json")):
+        for line in open(path):
+            if line.startswith("{") and '"roofline"' in line:
+                bench_line = json.loads(line)
+    wl_bytes = None
+    if workload in WORKLOADS:
+        T, heads, H, st, sh, wdt, res = WORKLOADS[workload]
+        sw = 4 if wdt == "f32" else 2
+        wl_bytes = {"fwd_kernel": fwd_bytes(T * heads, H, sw, res is True, res == "gate"),
+                    "bwd_kernel": bwd_bytes(T * heads, H, sw, False, res == "gate")}
+    out = [f"# rocprofv3 summary: workload {workload}", "",
+           "Commands (run from /tmp with TMPDIR=/tmp on one MI355X; R = repository root, OUT = an output "
+           "directory; the first run's stdout goes to OUT/ktrace.log):", "", "```", *profile_commands(workload, steps, warmup),
+           "```", "", "## Kernel statistics (--kernel-trace --stats)", "",
+           "| kernel | calls | average us | min us | max us |", "|---|---|---|---|---|"]
+    avg = {}
+    for r in stats:
+        k = key_of(r["Name"])
+        if k and k not in avg:
+            avg[k] = float(r["AverageNs"]) / 1e3
+        out.append(f"| `{r['Name'][:90]}` | {r['Calls']} | {float(r['AverageNs']) / 1e3:.2f} | "
+                   f"{float(r['MinNs']) / 1e3:.2f} | {float(r['MaxNs']) / 1e3:.2f} |")
+    if wl_bytes:
+        out += ["", "## Roofline (algorithmic bytes / duration / 8 TB/s)", "",
+                f"`all launches`: the --stats average over every launch of the process; `last run`: the trace's "
+                f"average over the {steps} steps whose launches bench.py brackets with HIP events (the last "
+                f"{steps} steps of the run); `bench events`: bench.py's own mean over those launches, from its JSON "
+                f"line in the same run (OUT/ktrace.log).  For the backward the row kernel and the reduce kernel "
+                f"(when the route has one) are added.", "",
+                "| op | algorithmic bytes | all launches us (frac) | last run us (frac) | bench events us (frac) |",
+                "|---|---|---|---|---|"]
+        ev = {}
+        if bench_line:
+            ev["fwd"] = bench_line["roofline"]["us_per_launch_mean"]
+            ev["bwd"] = bench_line["roofline_bwd"]["us_per_call_mean"]
+
+        def cell(t, nbytes):
+            return f"{t:.2f} ({nbytes / (t * 1e-6) / 8e12:.4f})" if t else "-"
+
+        for op, ks, nb in (("fwd", ("fwd_kernel",), wl_bytes["fwd_kernel"]),
+                           ("bwd", ("bwd_kernel", "bwd_cols_kernel", "dw_reduce_kernel"), wl_bytes["bwd_kernel"])):
+            t_all = sum(avg.get(k, 0.0) for k in ks)
+            t_last = sum(statistics.fmean(last_run[k]) for k in ks if k in last_run)
+            out.append(f"| {op} | {nb:,} | {cell(t_all, nb)} | {cell(t_last, nb)} | {cell(ev.get(op), nb)} |")
+    out += ["", "## HBM traffic per dispatch (--pmc FETCH_SIZE, WRITE_SIZE; KiB)", "",
+            f"Scale: a plain 1 GiB device copy (the first three copies of the process, `__amd_rocclr_copyBuffer`, "
+            f"1,048,576 KiB each way) reads FETCH_SIZE = {sum(fc) / len(fc):,.0f} KiB and WRITE_SIZE = "
+            f"{sum(wc) / len(wc):,.0f} KiB, so FETCH_SIZE is scaled by {fscale:.4f} and WRITE_SIZE by {wscale:.4f}.",
+            "", "| kernel | FETCH_SIZE raw | WRITE_SIZE raw | scaled bytes per dispatch | source hash |",
+            "|---|---|---|---|---|"]
+    rec = {"workload": workload, "fetch_scale": fscale, "write_scale": wscale, "kernels": {}, "trace_avg_us": avg,
+           "trace_last_run_avg_us": {k: statistics.fmean(v) for k, v in last_run.items()}}
+    for name in sorted(set(fetch) | set(write)):
+        k = key_of(name)
+        if not k:
+            continue
+        fb, wb = fetch.get(name, 0.0), write.get(name, 0.0)
+        total = int(round((fb * fscale + wb * wscale) * 1024))
+        out.append(f"| `{name[:90]}` | {fb:,.1f} | {wb:,.1f} | {total:,} | {source_hash(k)} |")
+        if k not in rec["kernels"]:
+            rec["kernels"][k] = {"traffic_bytes": total, "source_hash": source_hash(k), "kernel": name}
+    out += ["", "Machine-readable (read by bench.py; a source hash that no longer matches the sources means the "
+            "figure is stale):", "", "```json", json.dumps(rec, indent=1), "```", ""]
+    return "\n".join(out)
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default=DEFAULT_WORKLOAD, choices=sorted(WORKLOADS))
     ap.add_argument("--cold-reps", type=int, default=210,
                     help="cache-flushed launches per op, split over --cold-rounds interleaved rounds")
     ap.add_argument("--cold-rounds", type=int, default=3)
     ap.add_argument("--no-small-t", action="store_true", help="skip the small-T latency sweep")
+    ap.add_argument("--no-extra", action="store_true", help="skip the extra workloads (T65536_H4096_w32)")
     ap.add_argument("--shape-sweep", action="store_true",
                     help="also time every shape of the pages' latency tables (a few minutes)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--profile", action="store_true",
-                    help="only warmup + timed steps (for rocprofv3 runs), no per-op extras")
+                    help="only warmup + the two runs of timed steps (for rocprofv3 runs), no per-op extras")
     ap.add_argument("--span-sweep", metavar="SEQ",
                     help="run the pages' shapes as flush-delimited ops for a rocprofv3 kernel trace; "
                          "write the segment labels to SEQ and exit")
     ap.add_argument("--span-report", nargs=2, metavar=("TRACE_CSV", "SEQ"),
                     help="print per-shape median kernel spans from a --span-sweep trace and exit")
+    ap.add_argument("--profile-report", nargs=4, metavar=("OUT", "WORKLOAD", "STEPS", "WARMUP"),
+                    help="print the markdown summary of the three rocprofv3 runs under OUT and exit")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain 1 GiB device copy (reference for HBM counter scaling)")
     args = ap.parse_args()
@@ -505,6 +781,10 @@ def main():
     if args.span_report:
         rep = span_report(*args.span_report)
         print(json.dumps({"kernel_spans_us": rep}))
+        return
+    if args.profile_report:
+        o, w, k, wu = args.profile_report
+        print(profile_report(o, w, int(k), int(wu)))
         return
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -538,24 +818,14 @@ def main():
         log("copy calibration: 3 x copy of 1 GiB done")
     wl = Workload(args.workload)
     log(f"workload {wl.name}: R={wl.R} H={wl.H} w={wl.wdt} res={wl.res}")
-
-    # warmup + timed steps (deterministic backward), back to back
-    for _ in range(args.warmup):
-        wl.step(True)
-    torch.cuda.synchronize()
-    log(f"warmup {args.warmup} steps done")
-    t0 = time.perf_counter()
-    ev0 = torch.cuda.Event(enable_timing=True)
-    ev1 = torch.cuda.Event(enable_timing=True)
-    ev0.record()
-    for _ in range(args.steps):
-        wl.step(True)
-    ev1.record()
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    ms_per_step = ev0.elapsed_time(ev1) / args.steps
+    ms_per_step, fwd_us, bwd_us = measure_workload(wl, args)
+    flush = None if args.profile else torch.empty(1 << 28, dtype=torch.float32, device="cuda")  # 1 GiB
     value = wl.step_bytes / (ms_per_step * 1e-3) / 1e9
-    log(f"timed {args.steps} steps: {ms_per_step * 1e3:.1f} us/step, {value:.0f} GB/s (wall {wall:.3f}s)")
+    basis = (f"HIP events around each launch on the library's stream, mean over a second run of {args.steps} "
+             f"steps after the warm-up and the timed run ({len(fwd_us)} forward launches, {len(bwd_us)} backward "
+             f"calls); the committed rocprofv3 summary of bench.py --profile gives the kernel trace's average over "
+             f"the same launches beside it")
+    roof, roof_b = roofline_of(wl, fwd_us, bwd_us, basis)
 
     out = {
         "metric": "RMSNorm fwd/bwd/2xfwd+bwd \u00b5s and effective HBM GB/s (% of peak) at [T,H]",
@@ -573,47 +843,20 @@ def main():
         "dtype": "f32",
         "storage_dtype": "bf16",
         "accumulation": "f64 row sums and dw column sums",
-        "data": "synthetic (seeded N(0,1) x and dy, w = 1 + 0.1 N(0,1))",
+        "data": "synthetic (seeded N(0,1) x, r and dy, w = 1 + 0.1 N(0,1))",
         "config": {"workload": wl.name, "T": wl.T, "heads": wl.heads, "H": wl.H, "w_dtype": wl.wdt,
                    "residual": wl.res, "silu_gate": wl.gate,
                    "step": "fwd + fwd (recompute) + bwd (deterministic)",
                    "step_bytes": wl.step_bytes, "pct_of_peak": round(100 * value / PEAK_GBS, 2)},
+        "roofline": roof,
+        "roofline_bwd": roof_b,
+        "route": route_of(wl, rn),
     }
+    log(f"{wl.name}: {ms_per_step * 1e3:.1f} us/step, {value:.0f} GB/s; fwd frac {roof['frac']}, "
+        f"bwd frac {roof_b['frac']}")
 
     if not args.profile:
-        # per-op latency, cold caches; "fwd_aa" is the forward again, timed as
-        # if it were another implementation (the A/A floor of the method)
-        flush = torch.empty(1 << 28, dtype=torch.float32, device="cuda")  # 1 GiB
-        ops = {
-            "fwd": (wl.fwd, wl.fwd_bytes),
-            "fwd_aa": (wl.fwd, wl.fwd_bytes),
-            "bwd_det": (lambda: wl.bwd(True), wl.bwd_bytes),
-            "bwd_nondet": (lambda: wl.bwd(False), wl.bwd_bytes),
-            **({"bwd_det_dres": (lambda: wl.bwd(True, wl.dres), bwd_bytes(wl.R, wl.H, wl.sw, True))}
-               if wl.res else {}),
-            "step_det": (lambda: wl.step(True), wl.step_bytes),
-            "step_nondet": (lambda: wl.step(False), wl.step_bytes),
-        }
-        ops["step_det_graph"] = (graphed(lambda: wl.step(True)), wl.step_bytes)
-        for fn, _ in ops.values():
-            for _ in range(3):
-                fn()
-        reps = max(1, -(-args.cold_reps // args.cold_rounds))
-        raw = time_cold({k: v[0] for k, v in ops.items()}, args.cold_rounds, reps, flush)
-        lat = {}
-        for name, (_, nbytes) in ops.items():
-            c = summarize(raw[name])
-            c["gbs"] = round(nbytes / (c["median_us"] * 1e-6) / 1e9, 1)
-            c["pct_peak"] = round(100 * c["gbs"] / PEAK_GBS, 2)
-            c["bytes"] = nbytes
-            lat[name] = c
-            log(f"cold {name}: {c['median_us']:.1f} us  {c['gbs']:.0f} GB/s ({c['pct_peak']:.1f}%)")
-        lat["aa_floor_pct"] = round(100 * abs(lat["fwd"]["median_us"] - lat["fwd_aa"]["median_us"])
-                                    / lat["fwd"]["median_us"], 3)
-        # deterministic over non-deterministic backward time (> 1: non-det faster)
-        lat["mode_ratio_bwd"] = round(lat["bwd_det"]["median_us"] / lat["bwd_nondet"]["median_us"], 4)
-        out["latency_cold"] = lat
-
+        out["latency_cold"] = cold_latencies(wl, args, flush)
         if not args.no_small_t:
             t0 = time.time()
             out["small_t"] = shape_latencies(SMALL_T_SHAPES, flush, args.cold_rounds, 20)
@@ -622,39 +865,27 @@ def main():
             t0 = time.time()
             out["shape_sweep"] = shape_latencies(SWEEP_SHAPES, flush, args.cold_rounds, 20)
             log(f"shape sweep: {len(SWEEP_SHAPES)} shapes in {time.time() - t0:.1f}s")
-
-        # roofline of the dominant kernels: per-launch duration from HIP events
-        # around back-to-back launches on the stream the library uses
-        fwd_us = time_warm(wl.fwd, 40)
-        bwd_nd_us = time_warm(lambda: wl.bwd(False), 40)
-        bwd_d_us = time_warm(lambda: wl.bwd(True), 40)
-        # The forward kernel runs twice per step and takes the larger share
-        # of it; the backward (row kernel + fixed-order dw reduce) is shown
-        # beside it.
-        fwd_gbs = wl.fwd_bytes / (fwd_us * 1e-6) / 1e9
-        out["roofline"] = {"bound": "hbm", "kernel": "fwd_kernel", "achieved": round(fwd_gbs, 1),
-                           "peak": PEAK_GBS, "unit": "GB/s", "frac": round(fwd_gbs / PEAK_GBS, 4),
-                           "traffic": profiled_traffic(wl.name, "fwd_kernel"),
-                           "us_per_launch": round(fwd_us, 2), "bytes_per_launch": wl.fwd_bytes}
-        bwd_gbs = wl.bwd_bytes / (bwd_d_us * 1e-6) / 1e9
-        out["roofline_bwd"] = {"bound": "hbm", "kernel": "bwd_kernel + dw_reduce_kernel (deterministic)",
-                               "achieved": round(bwd_gbs, 1), "peak": PEAK_GBS, "unit": "GB/s",
-                               "frac": round(bwd_gbs / PEAK_GBS, 4),
-                               "traffic_row_kernel": profiled_traffic(wl.name, "bwd_kernel"),
-                               "us_per_call": round(bwd_d_us, 2), "bytes_per_call": wl.bwd_bytes,
-                               "nondet_us_per_call": round(bwd_nd_us, 2)}
-        log(f"warm fwd {fwd_us:.1f} us, bwd nondet {bwd_nd_us:.1f} us, bwd det {bwd_d_us:.1f} us")
-        route = {}
-        for det in (1, 0):
-            f, chunks = rn.rmsnorm_bwd_route(wl.T, wl.heads, wl.H, 1 if wl.wdt == "f32" else 0, wl.res, det)
-            route["det" if det else "nondet"] = {"form": "pair" if f == 0 else "atomic", "chunks": chunks}
-        out["route"] = route
-
         if not args.no_cpu_baseline:
             t0 = time.time()
             out["cpu_baseline"] = cpu_baseline(wl)
             log(f"cpu baseline: {out['cpu_baseline']['value']:.2f} GB/s on {out['cpu_baseline']['cores']} "
                 f"threads ({time.time() - t0:.1f}s)")
+        if not args.no_extra:
+            extra = {}
+            for name in EXTRA_WORKLOADS:
+                if name == wl.name:
+                    continue
+                xw = Workload(name)
+                ms, fu, bu = measure_workload(xw, args)
+                r1, r2 = roofline_of(xw, fu, bu, "as roofline.basis")
+                extra[name] = {"ms_per_step": round(ms, 5),
+                               "value": round(xw.step_bytes / (ms * 1e-3) / 1e9, 1), "unit": "GB/s",
+                               "roofline": r1, "roofline_bwd": r2, "route": route_of(xw, rn),
+                               "latency_cold": cold_latencies(xw, argparse.Namespace(
+                                   cold_reps=60, cold_rounds=args.cold_rounds), flush)}
+                del xw
+                torch.cuda.empty_cache()
+            out["other_workloads"] = extra
 
     print(json.dumps(out), flush=True)
 

@@ -94,22 +94,33 @@ int rmsnorm_fwd(const void* x, const void* residual, const void* w, int w_dtype,
                 double eps, int deterministic, void* stream);
 
 /*
- * Workspace bytes that rmsnorm_bwd needs for this shape (p1 #8208 page: the
- * facade exposes backward_workspace_bytes / backward_workspace).  A pure
- * function of its arguments; it makes no HIP call.  The size covers both
- * modes, so one workspace serves deterministic and non-deterministic calls
- * alike.  Returns 0 when the shape is invalid or unsupported.
+ * Workspace bytes that rmsnorm_bwd needs for these arguments (p1 #8208 page:
+ * the facade exposes backward_workspace_bytes / backward_workspace, which
+ * take the backward's arguments and its deterministic flag).
+ *   T, heads, H  the backward's shape (as for rmsnorm_bwd).
+ *   w_dtype      the weight's dtype (RMSN_W_BF16 or RMSN_W_F32).
+ *   residual     the dres pointer the backward will be given, or NULL; only
+ *                whether it is NULL matters (it is never dereferenced).
+ *   deterministic the backward's flag.
+ * The size is that of the route rmsnorm_bwd takes for the same arguments
+ * (rmsnorm_bwd_route), so a workspace sized for one mode may be too small
+ * for the other: size it with both flags (the larger) to share it.  A pure
+ * function of its arguments; it makes no HIP call.  Always at least the
+ * prepared part of rmsnorm_bwd_workspace_init; returns 0 when the shape or
+ * w_dtype is invalid or unsupported.
  */
-size_t rmsnorm_bwd_workspace_size(int64_t T, int64_t heads, int64_t H, int deterministic);
+size_t rmsnorm_bwd_workspace_size(int64_t T, int64_t heads, int64_t H, int w_dtype, const void* residual,
+                                  int deterministic);
 
 /*
  * Prepare a workspace for first use: zero-fills the part that the
- * non-deterministic backward keeps between calls (a ticket and an FP64 [H]
- * accumulator).  Every non-deterministic call leaves that part zero again, so
- * this is needed once per fresh allocation (or after a failed call).  A
- * workspace that is all zero bytes is already prepared.  A deterministic
- * call reads only what it wrote itself earlier in the same call, so it
- * needs no preparation and leaves the accumulator and ticket as it found them.
+ * non-deterministic backward keeps between calls (arrival tickets and an
+ * FP64 [H] accumulator).  Every non-deterministic call leaves that part zero
+ * again, so this is needed once per fresh allocation (or after a failed
+ * call).  A workspace that is all zero bytes is already prepared.  A
+ * deterministic call reads only what it wrote itself earlier in the same
+ * call, so it needs no preparation and leaves the tickets and accumulator
+ * as it found them.
  */
 int rmsnorm_bwd_workspace_init(void* workspace, size_t workspace_bytes, int64_t H, void* stream);
 
@@ -123,17 +134,22 @@ int rmsnorm_bwd_workspace_init(void* workspace, size_t workspace_bytes, int64_t 
  *   w, w_dtype  the forward's weight.
  *   residual  [T,heads,H] BF16 dres, the incoming gradient of h, or NULL; it
  *             is added to dx (dx is then the gradient of both x and r).
- *   dx        [T,heads,H] BF16 output.
+ *   dx        [T,heads,H] BF16 output; may be dy (in place).  Then the
+ *             column forms run their column tasks, which read dy of every
+ *             row, as a launch of their own before the row tasks that
+ *             overwrite it: one launch more, the same bits.
  *   dw        [H] FP32 output, overwritten (not accumulated into).
  *   workspace at least rmsnorm_bwd_workspace_size(...) bytes, prepared once
  *             by rmsnorm_bwd_workspace_init; must not be used by two calls
  *             at the same time.
- *   deterministic 1: each chunk of rows writes FP64 column partials and a
- *             second kernel sums them in a fixed order, so dw is bitwise
- *             reproducible for a given shape on any MI355X.
- *             0: the route may add the chunks' FP64 partials atomically;
- *             the measured MI355X route takes the fixed-order pair at every
- *             shape, as it is faster there (rmsnorm_bwd_route reports it).
+ *   deterministic 1: dw is summed in an order fixed by the shape alone (a
+ *             fixed-order pair, or the column form; rmsnorm_bwd_route reports
+ *             which), so it is bitwise reproducible for a given shape on any
+ *             MI355X, and the workspace may hold anything on entry.
+ *             0: the route may also take forms whose order of additions is
+ *             not fixed (atomic accumulation) or that keep arrival tickets
+ *             in the workspace's prepared part; dw is then reproducible only
+ *             within its error budget.  dx is the same in both modes.
  */
 int rmsnorm_bwd(const void* dy, const void* x, const float* rstd, const void* w, int w_dtype,
                 const void* residual, void* dx, float* dw,
@@ -152,10 +168,12 @@ int rmsnorm_bwd(const void* dy, const void* x, const float* rstd, const void* w,
  *   dx, dw = the plain backward's at the gated gradient e = dy * silu(g).
  * No residual.  g and dg are [T,heads,H] BF16 with the activations' strides;
  * dg may be g and dx may be dy.  silu is evaluated in FP32 (sigmoid within
- * ~4 units in the last place), so dx, dg and dw carry its relative error
+ * ~4 units in the last place while it is a normal number, and rounded once
+ * to the subnormal grid below that, down to g ~ -103; g = -inf gives
+ * silu = NaN, the formula's IEEE value), so dx, dg and dw carry its error
  * besides their own rounding; all other arithmetic is as in the plain
- * calls.  The workspace is the plain backward's (rmsnorm_bwd_workspace_size)
- * and the same rules apply.
+ * calls.  The workspace is the plain backward's
+ * (rmsnorm_bwd_workspace_size with residual NULL) and the same rules apply.
  */
 int rmsnorm_gated_fwd(const void* x, const void* gate, const void* w, int w_dtype, void* y, float* rstd,
                       int64_t T, int64_t heads, int64_t H, int64_t stride_t, int64_t stride_h,
@@ -169,24 +187,43 @@ int rmsnorm_gated_bwd(const void* dy, const void* x, const void* gate, const flo
 /*
  * Route inspection and override, for the route-table measurement and for
  * tests that cover both sides of a route edge (p3 #8293 commit message: its
- * pairs test exercises each edge from both sides).  A route names how the
- * backward reduces dw over rows:
+ * pairs test exercises each edge from both sides; p1 #8577 "Column-task
+ * launch": row-chunk and column-task workgroups in one launch).  A route
+ * names how the backward reduces dw over rows:
  *   form   RMSN_FORM_PAIR: each of `chunks` workgroups writes an FP64 column
  *          partial to the workspace and a second kernel sums them in a fixed
  *          order (deterministic; with chunks = 1 the one workgroup writes dw
- *          itself and there is no second kernel); RMSN_FORM_ATOMIC: the
- *          workgroups add their partials to an FP64 accumulator atomically
- *          and the last one to finish writes dw (one launch; order of
- *          additions not fixed).
- *   chunks number of workgroups of the row kernel, 1 .. 65536; workgroup c
- *          takes the row groups c, c + chunks, c + 2*chunks, ...
+ *          itself and there is no second kernel).
+ *          RMSN_FORM_ATOMIC: the workgroups add their partials to an FP64
+ *          accumulator atomically and the last one to finish writes dw (one
+ *          launch; order of additions not fixed; non-deterministic only).
+ *          RMSN_FORM_COLS: one launch of `chunks` row tasks, which form dx,
+ *          beside column tasks, which form dw for slices of 8 * col_vecs
+ *          columns straight from x, dy and rstd, each over all rows of its
+ *          slice (col_chunks = 1: dw written directly, no workspace beyond
+ *          the prepared part) or over one of col_chunks row blocks, whose
+ *          FP64 partials a second kernel sums in a fixed order.
+ *          Deterministic.
+ *          RMSN_FORM_COLS_TICKET: RMSN_FORM_COLS with col_chunks >= 2, where
+ *          the column task that finishes a slice last (a per-slice arrival
+ *          ticket in the prepared part) sums that slice's partials in the
+ *          fixed order: one launch; non-deterministic mode only (it needs
+ *          the prepared workspace).
+ *   chunks number of row-kernel workgroups (pair, atomic) or row tasks
+ *          (column forms), 1 .. 65536; workgroup c takes the row groups c,
+ *          c + chunks, c + 2*chunks, ...
+ *   col_chunks, col_vecs  column forms only (0 for the others): row blocks
+ *          per column slice, 1 .. 4096; 16-byte vectors per slice: 1, 2, 4
+ *          or 8.
  * The per-row work, and so dx, does not depend on the route.
  */
-enum rmsn_form { RMSN_FORM_PAIR = 0, RMSN_FORM_ATOMIC = 1 };
+enum rmsn_form { RMSN_FORM_PAIR = 0, RMSN_FORM_ATOMIC = 1, RMSN_FORM_COLS = 2, RMSN_FORM_COLS_TICKET = 3 };
 
 typedef struct rmsn_route {
     int32_t form;
     int32_t chunks;
+    int32_t col_chunks;
+    int32_t col_vecs;
 } rmsn_route;
 
 /* The route rmsnorm_bwd takes for these arguments.  Returns a status. */
@@ -197,7 +234,8 @@ int rmsnorm_bwd_route(int64_t T, int64_t heads, int64_t H, int w_dtype, int has_
 size_t rmsnorm_bwd_workspace_size_for_route(int64_t T, int64_t heads, int64_t H, rmsn_route route);
 
 /* rmsnorm_bwd with an explicit route.  deterministic = 1 requires the pair
- * form (RMSN_ERR_INVALID_ARG otherwise). */
+ * or the column form (RMSN_ERR_INVALID_ARG otherwise, and for any
+ * malformed route). */
 int rmsnorm_bwd_routed(const void* dy, const void* x, const float* rstd, const void* w, int w_dtype,
                        const void* residual, void* dx, float* dw,
                        void* workspace, size_t workspace_bytes,

@@ -27,6 +27,8 @@ RMSN_W_BF16 = 0
 RMSN_W_F32 = 1
 RMSN_FORM_PAIR = 0
 RMSN_FORM_ATOMIC = 1
+RMSN_FORM_COLS = 2
+RMSN_FORM_COLS_TICKET = 3
 RMSN_MAX_H = 16384
 
 # every symbol include/rmsnorm.h declares
@@ -45,7 +47,10 @@ EXPORTS = (
 
 
 class RmsnRoute(ctypes.Structure):
-    _fields_ = [("form", ctypes.c_int32), ("chunks", ctypes.c_int32)]
+    """(form, chunks, col_chunks, col_vecs); the last two are 0 except for
+    the column forms."""
+    _fields_ = [("form", ctypes.c_int32), ("chunks", ctypes.c_int32), ("col_chunks", ctypes.c_int32),
+                ("col_vecs", ctypes.c_int32)]
 
 
 class RmsnError(RuntimeError):
@@ -70,7 +75,7 @@ def lib() -> ctypes.CDLL:
     L.rmsnorm_fwd.argtypes = [vp, vp, vp, i32, vp, vp, vp, i64, i64, i64, i64, i64,
                               ctypes.c_double, i32, vp]
     L.rmsnorm_fwd.restype = i32
-    L.rmsnorm_bwd_workspace_size.argtypes = [i64, i64, i64, i32]
+    L.rmsnorm_bwd_workspace_size.argtypes = [i64, i64, i64, i32, vp, i32]
     L.rmsnorm_bwd_workspace_size.restype = ctypes.c_size_t
     L.rmsnorm_bwd_workspace_init.argtypes = [vp, ctypes.c_size_t, i64, vp]
     L.rmsnorm_bwd_workspace_init.restype = i32
@@ -227,8 +232,13 @@ def rmsnorm_fwd(x, w, eps: float = 1e-6, residual=None, deterministic: bool = Tr
 
 # ----------------------------------------------------------- backward ----
 
-def rmsnorm_bwd_workspace_size(T: int, heads: int, H: int, deterministic: bool = True) -> int:
-    return int(lib().rmsnorm_bwd_workspace_size(T, heads, H, int(bool(deterministic))))
+def rmsnorm_bwd_workspace_size(T: int, heads: int, H: int, w_dtype: int = RMSN_W_BF16,
+                               has_residual: bool = False, deterministic: bool = True) -> int:
+    """Bytes rmsnorm_bwd needs for these arguments (0 if they are invalid).
+    The C call takes the dres pointer itself; only whether it is NULL counts,
+    so a stand-in non-NULL address is passed for has_residual."""
+    res = ctypes.c_void_p(1) if has_residual else None
+    return int(lib().rmsnorm_bwd_workspace_size(T, heads, H, int(w_dtype), res, int(bool(deterministic))))
 
 
 def rmsnorm_bwd_workspace_init(workspace, H: int, stream=None):
@@ -238,10 +248,17 @@ def rmsnorm_bwd_workspace_init(workspace, H: int, stream=None):
     _check("rmsnorm_bwd_workspace_init", st_)
 
 
-def rmsnorm_bwd_workspace(T: int, heads: int, H: int, device, deterministic: bool = True, nbytes=None):
-    """A zero-filled (hence prepared) workspace tensor for rmsnorm_bwd."""
+def rmsnorm_bwd_workspace(T: int, heads: int, H: int, device, deterministic=None, nbytes=None,
+                          w_dtype: int = RMSN_W_BF16, has_residual: bool = False):
+    """A zero-filled (hence prepared) workspace tensor for rmsnorm_bwd.  With
+    deterministic=None it serves both modes (the larger of the two sizes)."""
     torch = _torch()
-    n = nbytes if nbytes is not None else rmsnorm_bwd_workspace_size(T, heads, H, deterministic)
+    if nbytes is not None:
+        n = nbytes
+    else:
+        modes = (True, False) if deterministic is None else (bool(deterministic),)
+        sizes = [rmsnorm_bwd_workspace_size(T, heads, H, w_dtype, has_residual, d) for d in modes]
+        n = 0 if min(sizes) == 0 else max(sizes)
     if n == 0:
         raise ValueError("unsupported shape")
     return torch.zeros(n, dtype=torch.uint8, device=device)
@@ -249,10 +266,11 @@ def rmsnorm_bwd_workspace(T: int, heads: int, H: int, device, deterministic: boo
 
 def rmsnorm_bwd_route(T: int, heads: int, H: int, w_dtype: int, has_residual: bool,
                       deterministic: bool):
+    """The route rmsnorm_bwd takes: (form, chunks, col_chunks, col_vecs)."""
     r = RmsnRoute()
     _check("rmsnorm_bwd_route", lib().rmsnorm_bwd_route(T, heads, H, int(w_dtype), int(bool(has_residual)),
                                                         int(bool(deterministic)), ctypes.byref(r)))
-    return int(r.form), int(r.chunks)
+    return int(r.form), int(r.chunks), int(r.col_chunks), int(r.col_vecs)
 
 
 def rmsnorm_bwd_workspace_size_for_route(T: int, heads: int, H: int, route) -> int:
@@ -285,7 +303,8 @@ def rmsnorm_bwd(dy, x, rstd, w, residual=None, deterministic: bool = True, *,
     is the incoming gradient of h (dres) or None.  Returns (dx, dw)."""
     (T, heads, H, st, sh), dx, dw = _bwd_args(dy, x, rstd, w, residual, dx, dw)
     if workspace is None:
-        workspace = rmsnorm_bwd_workspace(T, heads, H, x.device, deterministic)
+        workspace = rmsnorm_bwd_workspace(T, heads, H, x.device, deterministic, w_dtype=_w_dtype(w),
+                                          has_residual=residual is not None)
     _workspace(workspace, x.device)
     st_ = lib().rmsnorm_bwd(_ptr(dy), _ptr(x), _ptr(rstd), _ptr(w), _w_dtype(w), _ptr(residual),
                             _ptr(dx), _ptr(dw), _ptr(workspace),
@@ -297,7 +316,8 @@ def rmsnorm_bwd(dy, x, rstd, w, residual=None, deterministic: bool = True, *,
 
 def rmsnorm_bwd_routed(dy, x, rstd, w, route, residual=None, deterministic: bool = True, *,
                        dx=None, dw=None, workspace=None, stream=None):
-    """rmsnorm_bwd with an explicit (form, chunks) route."""
+    """rmsnorm_bwd with an explicit route: (form, chunks) for the pair and
+    atomic forms, (form, chunks, col_chunks, col_vecs) for the column forms."""
     (T, heads, H, st, sh), dx, dw = _bwd_args(dy, x, rstd, w, residual, dx, dw)
     if workspace is None:
         workspace = rmsnorm_bwd_workspace(T, heads, H, x.device, deterministic,
@@ -345,7 +365,7 @@ def rmsnorm_gated_bwd(dy, x, g, rstd, w, deterministic: bool = True, *, dx=None,
     _act(dg, "dg", x)
     _same_geometry(x, dg, "dg")
     if workspace is None:
-        workspace = rmsnorm_bwd_workspace(T, heads, H, x.device, deterministic)
+        workspace = rmsnorm_bwd_workspace(T, heads, H, x.device, deterministic, w_dtype=_w_dtype(w))
     _workspace(workspace, x.device)
     _check("rmsnorm_gated_bwd", lib().rmsnorm_gated_bwd(
         _ptr(dy), _ptr(x), _ptr(g), _ptr(rstd), _ptr(w), _w_dtype(w), _ptr(dx), _ptr(dg), _ptr(dw),

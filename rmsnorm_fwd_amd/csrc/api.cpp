@@ -63,21 +63,13 @@ int cu_count()
 
 int status_of(hipError_t e) { return e == hipSuccess ? RMSN_OK : RMSN_ERR_HIP; }
 
-int check_route(const Shape& s, const rmsn_route& r, int deterministic)
-{
-    if (r.form != RMSN_FORM_PAIR && r.form != RMSN_FORM_ATOMIC) return RMSN_ERR_INVALID_ARG;
-    if (deterministic && r.form != RMSN_FORM_PAIR) return RMSN_ERR_INVALID_ARG;
-    (void)s;
-    if (r.chunks < 1 || r.chunks > kMaxChunks) return RMSN_ERR_INVALID_ARG;
-    return RMSN_OK;
-}
+BwdRoute internal(const rmsn_route& r) { return BwdRoute{r.form, r.chunks, r.col_chunks, r.col_vecs}; }
 
 int bwd_impl(const void* dy, const void* x, const float* rstd, const void* w, int w_dtype,
-             const void* dres, void* dx, float* dw, void* workspace, size_t workspace_bytes,
-             const Shape& s, const rmsn_route& route, hipStream_t stream,
+             const void* dres, void* dx, float* dw, void* workspace,
+             const Shape& s, const BwdRoute& r, hipStream_t stream,
              const void* gate = nullptr, void* dgate = nullptr)
 {
-    const BwdRoute r{route.form, route.chunks};
     if (s.R == 0) return status_of(launch_fill_zero(dw, s.H * 4, stream));
 
     const int layout = pick_layout(kBwdLayouts, kNumBwdLayouts, s.H);
@@ -94,6 +86,7 @@ int bwd_impl(const void* dy, const void* x, const float* rstd, const void* w, in
     char* ws = static_cast<char*>(workspace);
     p.ticket = reinterpret_cast<unsigned*>(ws);
     p.acc = reinterpret_cast<double*>(ws + ws_acc_offset());
+    p.slice_ticket = reinterpret_cast<unsigned*>(ws + ws_slice_ticket_offset(s.H));
     p.part = reinterpret_cast<double*>(ws + ws_part_offset(s.H));
     p.rows = make_row_map(s.heads, s.st, s.sh);
     p.R = (int)s.R;
@@ -102,7 +95,28 @@ int bwd_impl(const void* dy, const void* x, const float* rstd, const void* w, in
     p.form = r.form;
     p.direct_dw = r.form == FORM_PAIR && r.chunks == 1;
     p.inv_h = 1.0 / (double)s.H;
-    hipError_t e = launch_bwd(layout, w_dtype == RMSN_W_F32, p, stream);
+    const bool w32 = w_dtype == RMSN_W_F32;
+    if (r.form == FORM_COLS || r.form == FORM_COLS_TICKET) {
+        p.col_chunks = r.col_chunks;
+        p.col_vecs = r.col_vecs;
+        p.slices = (int)col_slices(s.H, r.col_vecs);
+        p.col_tasks = p.slices * r.col_chunks;
+        // In place (dx over dy, or dg over the gate) the column tasks, which
+        // read dy and the gate of every row, run first as a launch of their
+        // own and the row tasks after them: the same kernels and order of
+        // sums, so the same bits.
+        const bool in_place = dx == dy || (gate && dgate == gate);
+        hipError_t e = launch_bwd_cols(layout, w32, p, !in_place, stream);
+        if (e != hipSuccess) return RMSN_ERR_HIP;
+        if (r.form == FORM_COLS && r.col_chunks > 1) e = launch_dw_reduce(p.part, r.col_chunks, p.H, dw, stream);
+        if (e != hipSuccess) return RMSN_ERR_HIP;
+        if (in_place) {
+            p.col_tasks = 0;
+            e = launch_bwd_cols(layout, w32, p, true, stream);
+        }
+        return status_of(e);
+    }
+    hipError_t e = launch_bwd(layout, w32, p, stream);
     if (e != hipSuccess) return RMSN_ERR_HIP;
     if (r.form == FORM_PAIR && !p.direct_dw) e = launch_dw_reduce(p.part, p.chunks, p.H, dw, stream);
     return status_of(e);
@@ -193,27 +207,21 @@ int rmsnorm_gated_fwd(const void* x, const void* gate, const void* w, int w_dtyp
                     stream);
 }
 
-size_t rmsnorm_bwd_workspace_size(int64_t T, int64_t heads, int64_t H, int deterministic)
+size_t rmsnorm_bwd_workspace_size(int64_t T, int64_t heads, int64_t H, int w_dtype, const void* residual,
+                                  int deterministic)
 {
-    (void)deterministic;  // one layout serves both modes
+    if (w_dtype != RMSN_W_BF16 && w_dtype != RMSN_W_F32) return 0;
     if (!rows_ok(T, heads) || H < 1 || H % 8 != 0 || H > RMSN_MAX_H) return 0;
     const int64_t R = T * heads;
-    size_t best = ws_part_offset(H);
-    for (int det = 0; det <= 1; ++det)
-        for (int w32 = 0; w32 <= 1; ++w32)
-            for (int res = 0; res <= 1; ++res) {
-                const size_t b = ws_bytes_for(R, H, default_bwd_route(R, H, w32 != 0, res != 0, det != 0));
-                if (b > best) best = b;
-            }
-    return best;
+    return ws_bytes_for(R, H, default_bwd_route(R, H, w_dtype == RMSN_W_F32, residual != nullptr, deterministic != 0));
 }
 
 size_t rmsnorm_bwd_workspace_size_for_route(int64_t T, int64_t heads, int64_t H, rmsn_route route)
 {
     if (!rows_ok(T, heads) || H < 1 || H % 8 != 0 || H > RMSN_MAX_H) return 0;
-    if (route.chunks < 1 || route.chunks > kMaxChunks) return 0;
-    if (route.form != RMSN_FORM_PAIR && route.form != RMSN_FORM_ATOMIC) return 0;
-    return ws_bytes_for(T * heads, H, BwdRoute{route.form, route.chunks});
+    const BwdRoute r = internal(route);
+    if (!route_valid(r, false)) return 0;
+    return ws_bytes_for(T * heads, H, r);
 }
 
 int rmsnorm_bwd_workspace_init(void* workspace, size_t workspace_bytes, int64_t H, void* stream)
@@ -235,6 +243,8 @@ int rmsnorm_bwd_route(int64_t T, int64_t heads, int64_t H, int w_dtype, int has_
     const BwdRoute r = default_bwd_route(T * heads, H, w_dtype == RMSN_W_F32, has_residual != 0, deterministic != 0);
     out->form = r.form;
     out->chunks = r.chunks;
+    out->col_chunks = r.col_chunks;
+    out->col_vecs = r.col_vecs;
     return RMSN_OK;
 }
 
@@ -249,12 +259,10 @@ int rmsnorm_bwd_routed(const void* dy, const void* x, const float* rstd, const v
     if (st != RMSN_OK) return st;
     st = check_bwd_args(dy, x, rstd, w, w_dtype, residual, dx, dw, workspace, s);
     if (st != RMSN_OK) return st;
-    st = check_route(s, route, deterministic);
-    if (st != RMSN_OK) return st;
-    if (s.R > 0 && workspace_bytes < ws_bytes_for(s.R, s.H, BwdRoute{route.form, route.chunks}))
-        return RMSN_ERR_WORKSPACE;
-    return bwd_impl(dy, x, rstd, w, w_dtype, residual, dx, dw, workspace, workspace_bytes, s, route,
-                    static_cast<hipStream_t>(stream));
+    const BwdRoute r = internal(route);
+    if (!route_valid(r, deterministic != 0)) return RMSN_ERR_INVALID_ARG;
+    if (s.R > 0 && workspace_bytes < ws_bytes_for(s.R, s.H, r)) return RMSN_ERR_WORKSPACE;
+    return bwd_impl(dy, x, rstd, w, w_dtype, residual, dx, dw, workspace, s, r, static_cast<hipStream_t>(stream));
 }
 
 int rmsnorm_bwd(const void* dy, const void* x, const float* rstd, const void* w, int w_dtype,
@@ -269,11 +277,10 @@ int rmsnorm_bwd(const void* dy, const void* x, const float* rstd, const void* w,
     st = check_bwd_args(dy, x, rstd, w, w_dtype, residual, dx, dw, workspace, s);
     if (st != RMSN_OK) return st;
     const BwdRoute r = default_bwd_route(s.R, s.H, w_dtype == RMSN_W_F32, residual != nullptr, deterministic != 0);
-    const rmsn_route route{r.form, r.chunks};
     if (s.R > 0 && workspace_bytes < ws_bytes_for(s.R, s.H, r)) return RMSN_ERR_WORKSPACE;
-    return bwd_impl(dy, x, rstd, w, w_dtype, residual, dx, dw, workspace, workspace_bytes, s, route,
-                    static_cast<hipStream_t>(stream));
+    return bwd_impl(dy, x, rstd, w, w_dtype, residual, dx, dw, workspace, s, r, static_cast<hipStream_t>(stream));
 }
+
 
 int rmsnorm_gated_bwd(const void* dy, const void* x, const void* gate, const float* rstd, const void* w,
                       int w_dtype, void* dx, void* dgate, float* dw, void* workspace, size_t workspace_bytes,
@@ -288,10 +295,9 @@ int rmsnorm_gated_bwd(const void* dy, const void* x, const void* gate, const flo
     if (s.R > 0 && (!gate || !dgate)) return RMSN_ERR_INVALID_ARG;
     if (s.R > 0 && (!aligned(gate, 16) || !aligned(dgate, 16))) return RMSN_ERR_MISALIGNED;
     const BwdRoute r = default_bwd_route(s.R, s.H, w_dtype == RMSN_W_F32, false, deterministic != 0);
-    const rmsn_route route{r.form, r.chunks};
     if (s.R > 0 && workspace_bytes < ws_bytes_for(s.R, s.H, r)) return RMSN_ERR_WORKSPACE;
-    return bwd_impl(dy, x, rstd, w, w_dtype, nullptr, dx, dw, workspace, workspace_bytes, s, route,
-                    static_cast<hipStream_t>(stream), gate, dgate);
+    return bwd_impl(dy, x, rstd, w, w_dtype, nullptr, dx, dw, workspace, s, r, static_cast<hipStream_t>(stream),
+                    gate, dgate);
 }
 
 const char* rmsnorm_status_string(int status)

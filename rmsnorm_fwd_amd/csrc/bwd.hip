@@ -30,6 +30,16 @@
 //                that draws the last arrival ticket writes dw and zeroes the
 //                accumulator and ticket -- one launch, no waiting.
 //
+// Column forms (bwd_cols_kernel).  dw needs no row dot: dw_j = sum over rows
+// of dy_j * u_j * rstd, all three inputs of the backward.  So one launch runs
+// two kinds of workgroup side by side: row tasks form dx (the row kernel's
+// per-row work, without column sums) and column tasks form dw for a slice of
+// 8 * col_vecs columns, reading that slice of every row (or of a block of
+// rows) again.  No workgroup waits for another and no partial leaves the
+// chip when one column task covers all rows of its slice; with col_chunks
+// row blocks per slice the blocks' FP64 partials are summed in a fixed
+// order, by the reduce kernel or by the slice's last-arriving column task.
+//
 // SiLU gate (GATE).  With a gate g the gradient reaching the normalised row
 // is e = dy * silu(g): x*dy*silu(g) is still exact in FP64 (16 + 24 bits),
 // so S, dw and dx follow the same arithmetic with e in place of dy, and the
@@ -100,29 +110,27 @@ __device__ __forceinline__ void bwd_load(BwdTile<U, V, DRES, GATE>& t, const Bwd
         }
 }
 
-template <int LPR, int V, int U, bool WF32, bool DRES, bool GATE>
-__global__ void __launch_bounds__(block_of(LPR)) bwd_kernel(BwdParams p)
+// The row work of workgroup `chunk` of `nchunks`: row groups chunk,
+// chunk + nchunks, ... (interleaved, so that at any moment all workgroups
+// stream neighbouring rows, which keeps the HBM pages they touch together --
+// measured 1.1-1.25x over contiguous chunks of rows on MI355X).  Writes dx
+// (and dg) for those rows; with DW it also adds each row's dy * xhat into
+// the lane's column sums acc (which it first sets to zero).
+template <int LPR, int V, int U, bool WF32, bool DRES, bool GATE, bool DW>
+__device__ __forceinline__ void bwd_rows(const BwdParams& p, int chunk, int nchunks, double (&acc)[V][8])
 {
     constexpr int BLOCK = block_of(LPR);
     constexpr int SLOTS = BLOCK / LPR;
     constexpr int W = LPR > 64 ? LPR / 64 : 1;
     constexpr int RPI = SLOTS * U;
     __shared__ double red[2][RPI][W];
-    __shared__ int last_block;
-    extern __shared__ double slot_part[];  // [wavefronts][H] when SLOTS > 1
 
     const int tid = threadIdx.x;
     const int g = tid % LPR;
     const int slot = tid / LPR;
-    const int H = p.H;
-    const LaneVectors<V> lv(g, LPR, H >> 3);
-    const int chunk = blockIdx.x;
-    // Workgroup `chunk` takes the row groups chunk, chunk + chunks, ...:
-    // at any moment all workgroups stream neighbouring rows, which keeps the
-    // HBM pages they touch together (measured: 1.1-1.25x over contiguous
-    // chunks of rows on MI355X).
+    const LaneVectors<V> lv(g, LPR, p.H >> 3);
     const int first = chunk * RPI;
-    const int step = p.chunks * RPI;
+    const int step = nchunks * RPI;
     const int row1 = p.R;
 
     double w64[V][8];
@@ -140,12 +148,12 @@ __global__ void __launch_bounds__(block_of(LPR)) bwd_kernel(BwdParams p)
 #pragma unroll
         for (int e = 0; e < 8; ++e) w64[v][e] = lv.ok[v] ? (double)wv[e] : 0.0;
     }
-
-    double acc[V][8];
+    if constexpr (DW) {
 #pragma unroll
-    for (int v = 0; v < V; ++v)
+        for (int v = 0; v < V; ++v)
 #pragma unroll
-        for (int e = 0; e < 8; ++e) acc[v][e] = 0.0;
+            for (int e = 0; e < 8; ++e) acc[v][e] = 0.0;
+    }
 
     // Gated rows of one vector per lane load the workgroup's next rows while
     // the current ones are reduced (a second register tile): their
@@ -190,7 +198,7 @@ __global__ void __launch_bounds__(block_of(LPR)) bwd_kernel(BwdParams p)
                     // x * dy is exact in FP32; times silu(g) (24 bits) still exact in FP64
                     double pd = (double)(xf[e] * df[e]);
                     if constexpr (GATE) pd *= (double)sg[e];
-                    acc[v][e] = __builtin_fma(pd, rho[u], acc[v][e]);
+                    if constexpr (DW) acc[v][e] = __builtin_fma(pd, rho[u], acc[v][e]);
                     S[u] = __builtin_fma(pd, w64[v][e], S[u]);
                 }
             }
@@ -236,6 +244,25 @@ __global__ void __launch_bounds__(block_of(LPR)) bwd_kernel(BwdParams p)
             if (base + step < row1) cur = nxt;
         }
     }
+}
+
+template <int LPR, int V, int U, bool WF32, bool DRES, bool GATE>
+__global__ void __launch_bounds__(block_of(LPR)) bwd_kernel(BwdParams p)
+{
+    constexpr int BLOCK = block_of(LPR);
+    constexpr int SLOTS = BLOCK / LPR;
+    __shared__ int last_block;
+    extern __shared__ double slot_part[];  // [wavefronts][H] when SLOTS > 1
+
+    const int chunk = blockIdx.x;
+    double acc[V][8];
+    bwd_rows<LPR, V, U, WF32, DRES, GATE, true>(p, chunk, p.chunks, acc);
+
+    const int tid = threadIdx.x;
+    const int g = tid % LPR;
+    const int slot = tid / LPR;
+    const int H = p.H;
+    const LaneVectors<V> lv(g, LPR, H >> 3);
 
     // ---- chunk sum of dw ----------------------------------------------
     if constexpr (SLOTS > 1) {
@@ -313,6 +340,140 @@ __global__ void __launch_bounds__(block_of(LPR)) bwd_kernel(BwdParams p)
             if (tid == 0) __hip_atomic_store(p.ticket, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         }
     }
+}
+
+// ----------------------------------------------------- column forms ----
+// Column task `task` of a column-form launch: slice s = task % slices covers
+// the columns [8 col_vecs s, 8 col_vecs (s + 1)) (the last slice may end
+// early), row block k = task / slices the rows [k rpc, (k + 1) rpc) with
+// rpc = ceil(R / col_chunks).  Lane l reads vector l % col_vecs of the slice
+// in rows q, q + NQ, ... of the block (q = l / col_vecs, NQ = BLOCK /
+// col_vecs), four rows in flight, and adds dy * u * rstd (dy * silu(g) * u *
+// rstd with a gate) in FP64 from exact products, as the row kernel does.
+// Lanes of one vector are then added by a butterfly of lane exchanges inside
+// each wavefront and the wavefronts' sums through LDS in wavefront order: a
+// fixed order that depends only on R, H, col_chunks, col_vecs and BLOCK.
+template <int BLOCK, bool GATE>
+__device__ __forceinline__ void dw_column_task(const BwdParams& p, int task)
+{
+    constexpr int W = BLOCK / 64;
+    constexpr int B = 4;  // rows per lane in flight
+    __shared__ double cs[W][64];
+    __shared__ int last_task;
+
+    const int tid = threadIdx.x;
+    const int VC = p.col_vecs;
+    const int lg = __builtin_ctz((unsigned)VC);
+    const int v = tid & (VC - 1);
+    const int q = tid >> lg;
+    const int NQ = BLOCK >> lg;
+    const int s = task % p.slices;
+    const int k = task / p.slices;
+    const int nv = p.H >> 3;
+    const int vec = s * VC + v;
+    const int col = 8 * (vec < nv ? vec : nv - 1);  // lanes past the row's end re-read its last vector
+    const int rpc = (p.R + p.col_chunks - 1) / p.col_chunks;
+    const int r0 = k * rpc;
+    const int r1 = r0 + rpc < p.R ? r0 + rpc : p.R;
+
+    double acc[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) acc[e] = 0.0;
+    for (int base = r0 + q; base < r1; base += B * NQ) {
+        bool ok[B];
+        float rho[B];
+        uint4 xv[B], dv[B], gv[GATE ? B : 1];
+#pragma unroll
+        for (int b = 0; b < B; ++b) {
+            const int r = base + b * NQ;
+            ok[b] = r < r1;
+            const int rr = ok[b] ? r : base;
+            const int64_t off = row_offset(rr, p.rows) + col;
+            rho[b] = p.rstd[rr];
+            xv[b] = ld16(p.x + off);
+            dv[b] = ld16(p.dy + off);
+            if constexpr (GATE) gv[b] = ld16(p.g + off);
+        }
+#pragma unroll
+        for (int b = 0; b < B; ++b) {
+            float xf[8], df[8];
+            unpack8(xv[b], xf);
+            unpack8(dv[b], df);
+            float gf[8];
+            if constexpr (GATE) unpack8(gv[b], gf);
+            const double rh = (double)rho[b];
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                double pd = (double)(xf[e] * df[e]);
+                if constexpr (GATE) pd *= (double)(gf[e] * sigmoid_f32(gf[e]));
+                const double a = __builtin_fma(pd, rh, acc[e]);
+                acc[e] = ok[b] ? a : acc[e];
+            }
+        }
+    }
+    for (int off = VC; off < 64; off <<= 1)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) acc[e] += __shfl_xor(acc[e], off);
+    const int wave = tid >> 6;
+    if ((tid & 63) < VC) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) cs[wave][8 * v + e] = acc[e];
+    }
+    __syncthreads();
+    const int c = tid;                  // column within the slice (threads 0 .. 8 VC - 1)
+    const int cc = 8 * s * VC + c;      // column of H
+    const bool mine = c < 8 * VC && cc < p.H;
+    double t = 0.0;
+    if (mine) {
+        t = cs[0][c];
+#pragma unroll
+        for (int w = 1; w < W; ++w) t += cs[w][c];
+    }
+    if (p.col_chunks == 1) {
+        if (mine) p.dw[cc] = (float)t;
+        return;
+    }
+    if (mine) p.part[(int64_t)k * p.H + cc] = t;
+    if (p.form != FORM_COLS_TICKET) return;
+    // Ticket form: publish the block's partial (agent-scope fence), then take
+    // the slice's arrival ticket; the task that draws the last one sums the
+    // slice's col_chunks partials in block order, writes dw and clears the
+    // ticket.  No task waits for another.
+    __threadfence();
+    __syncthreads();
+    if (tid == 0) {
+        const unsigned n = __hip_atomic_fetch_add(p.slice_ticket + s, 1u, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
+        last_task = n == (unsigned)(p.col_chunks - 1);
+    }
+    __syncthreads();
+    if (!last_task) return;
+    __threadfence();
+    if (mine) {
+        double a = 0.0;
+        for (int kk = 0; kk < p.col_chunks; ++kk) a += p.part[(int64_t)kk * p.H + cc];
+        p.dw[cc] = (float)a;
+    }
+    if (tid == 0) __hip_atomic_store(p.slice_ticket + s, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// Column-form launch: workgroups [0, col_tasks) are column tasks (col_tasks
+// = slices * col_chunks, or 0 for a launch of row tasks alone), the rest
+// (p.chunks of them) row tasks that form dx with one row per row group and
+// iteration.  A row's arithmetic is the row kernel's (same lanes and vectors
+// per row), so dx is bitwise the same in every form.  In place (dx = dy, or
+// dg = g) the caller runs the column tasks and the row tasks as two launches
+// in that order: column tasks read dy (and g) of rows whose row tasks are
+// other workgroups.
+template <int LPR, int V, bool WF32, bool DRES, bool GATE>
+__global__ void __launch_bounds__(block_of(LPR)) bwd_cols_kernel(BwdParams p)
+{
+    const int ncol = p.col_tasks;
+    if ((int)blockIdx.x < ncol) {
+        dw_column_task<block_of(LPR), GATE>(p, blockIdx.x);
+        return;
+    }
+    double none[V][8];
+    bwd_rows<LPR, V, 1, WF32, DRES, GATE, false>(p, blockIdx.x - ncol, p.chunks, none);
 }
 
 __global__ void __launch_bounds__(kReduceCols * kReduceGroups)
@@ -422,6 +583,46 @@ hipError_t launch_bwd(int layout, bool w_f32, const BwdParams& p, hipStream_t s)
         return p.direct_dw ? bwd_direct<l, vv, uu>(w_f32, p, s) : bwd_dispatch<l, vv, uu>(w_f32, p, s);
         RMSN_BWD_LAYOUTS(RMSN_BWD_CASE)
 #undef RMSN_BWD_CASE
+    default: return hipErrorInvalidValue;
+    }
+}
+
+template <int LPR, int V, bool WF32, bool DRES, bool GATE>
+static hipError_t bwd_cols_t(const BwdParams& p, bool rows, hipStream_t s)
+{
+    const int grid = p.col_tasks + (rows ? p.chunks : 0);
+    if (grid < 1) return hipSuccess;
+    hipLaunchKernelGGL((bwd_cols_kernel<LPR, V, WF32, DRES, GATE>), dim3(grid), dim3(block_of(LPR)), 0, s, p);
+    return hipGetLastError();
+}
+
+template <int LPR, int V, bool DRES, bool GATE>
+static hipError_t bwd_cols_w(bool w_f32, const BwdParams& p, bool rows, hipStream_t s)
+{
+    return w_f32 ? bwd_cols_t<LPR, V, true, DRES, GATE>(p, rows, s) : bwd_cols_t<LPR, V, false, DRES, GATE>(p, rows, s);
+}
+
+// Gated rows of three vectors per lane run as rows of three times the lanes,
+// as in the row kernel (same row order).
+template <int LPR, int V>
+static hipError_t bwd_cols_dispatch(bool w_f32, const BwdParams& p, bool rows, hipStream_t s)
+{
+    if (p.dres) return bwd_cols_w<LPR, V, true, false>(w_f32, p, rows, s);
+    if (p.g) {
+        if constexpr (RMSN_GATED_WIDE_V3 && V == 3 && LPR <= 256)
+            return bwd_cols_w<3 * LPR, 1, false, true>(w_f32, p, rows, s);
+        else return bwd_cols_w<LPR, V, false, true>(w_f32, p, rows, s);
+    }
+    return bwd_cols_w<LPR, V, false, false>(w_f32, p, rows, s);
+}
+
+hipError_t launch_bwd_cols(int layout, bool w_f32, const BwdParams& p, bool rows, hipStream_t s)
+{
+    switch (layout) {
+#define RMSN_BWD_COLS_CASE(id, mh, l, vv, uu, kk) \
+    case id: return bwd_cols_dispatch<l, vv>(w_f32, p, rows, s);
+        RMSN_BWD_LAYOUTS(RMSN_BWD_COLS_CASE)
+#undef RMSN_BWD_COLS_CASE
     default: return hipErrorInvalidValue;
     }
 }

@@ -40,20 +40,31 @@ __device__ __forceinline__ uint32_t pack_bf16x2_from_f64(double lo, double hi)
 // t = -g * log2(e) carried as a rounded product p plus its error (an FMA
 // gives the product's rounding error exactly; log2(e)'s own tail is added),
 // so the hardware 2^p (v_exp_f32, 1 unit) is corrected by 2^lo ~ 1 + lo ln 2.
-// p is clamped to [-126, 126]: beyond it sigmoid is 1, or below 2^-126 and
-// only adds below 1e-36 to silu.  The reciprocal is v_rcp_f32 (1 unit), so
-// sigmoid is within ~4 units in the last place over the whole range.
+// For p > 64 (g < -44.4) numerator and denominator are scaled by 2^-64:
+// sigmoid = 2^-64 / (2^-64 + 2^(p-64)), the final 2^-64 applied by ldexp,
+// which rounds once into the subnormal range.  So 2^p never overflows and
+// sigmoid(g) follows e^g down to FP32's smallest subnormal (g near -103)
+// instead of stopping at 2^-126.  g is first clamped to [-128, 128]: beyond
+// that sigmoid is 1, or rounds to 0 either way.  The reciprocal is v_rcp_f32
+// (1 unit).  Relative error: ~4 units in the last place while sigmoid is a
+// normal FP32 number; below 2^-126 (g < -87.3) the result is the correctly
+// scaled value rounded once to the subnormal grid (absolute error <= 2^-149
+// plus the same ~4 units relative).  Infinite g gives sigmoid 1 or 0, so
+// silu(-inf) = -inf * 0 is NaN, as the formula g * sigmoid(g) reads in IEEE
+// arithmetic.
 __device__ __forceinline__ float sigmoid_f32(float g)
 {
     constexpr float kL2eHi = 1.44269502162933349609375f;   // log2(e) rounded to float
     constexpr float kL2eLo = 1.925963033500011e-08f;        // log2(e) - kL2eHi
     constexpr float kLn2 = 0.693147180559945309f;
-    const float p = -g * kL2eHi;
-    const float lo = __builtin_fmaf(-g, kL2eLo, __builtin_fmaf(-g, kL2eHi, -p));
-    const float pc = __builtin_amdgcn_fmed3f(p, -126.0f, 126.0f);
-    const float e0 = __builtin_amdgcn_exp2f(pc);
-    const float e = pc == p ? __builtin_fmaf(e0, lo * kLn2, e0) : e0;
-    return __builtin_amdgcn_rcpf(1.0f + e);
+    const float gc = __builtin_amdgcn_fmed3f(g, -128.0f, 128.0f);
+    const float p = -gc * kL2eHi;
+    const float lo = __builtin_fmaf(-gc, kL2eLo, __builtin_fmaf(-gc, kL2eHi, -p));
+    const bool big = p > 64.0f;
+    const float e0 = __builtin_amdgcn_exp2f(p - (big ? 64.0f : 0.0f));
+    const float e = __builtin_fmaf(e0, lo * kLn2, e0);
+    const float r = __builtin_amdgcn_rcpf((big ? 0x1p-64f : 1.0f) + e);
+    return __builtin_amdgcn_ldexpf(r, big ? -64 : 0);
 }
 
 __device__ __forceinline__ void unpack8(const uint4& v, float f[8])

@@ -55,14 +55,19 @@ struct BwdParams {
     uint16_t* dg;         // gate gradient (when g != nullptr)
     uint16_t* dx;
     float* dw;
-    double* part;         // [P,H] FP64 chunk partials (pair form)
+    double* part;         // [P,H] FP64 partials (pair form: P = chunks; column forms: P = col_chunks)
     double* acc;          // [H] FP64 accumulator (atomic form), zero on entry and exit
     unsigned* ticket;     // arrival counter (atomic form), zero on entry and exit
+    unsigned* slice_ticket;  // [slices] arrival counters (column ticket form), zero on entry and exit
     RowMap rows;
     int R, H;
-    int chunks;           // workgroups; workgroup c takes row groups c, c + chunks, ...
-    int form;             // FORM_PAIR or FORM_ATOMIC (route.h)
+    int chunks;           // row workgroups; workgroup c takes row groups c, c + chunks, ...
+    int form;             // FORM_* (route.h)
     int direct_dw;        // pair form with one chunk: write dw, skip the reduce
+    int col_chunks;       // column forms: row blocks per column slice
+    int col_vecs;         // column forms: 16-byte vectors per column slice (1, 2, 4 or 8)
+    int slices;           // column forms: column slices, ceil(H / (8 col_vecs))
+    int col_tasks;        // column forms: column tasks at the start of this launch's grid (0: row tasks only)
     double inv_h;
 };
 
@@ -72,7 +77,11 @@ struct BwdParams {
 // FWD_RES_LONG only with a residual).
 hipError_t launch_fwd(int table, int layout, bool w_f32, const FwdParams& p, int grid, hipStream_t s);
 hipError_t launch_bwd(int layout, bool w_f32, const BwdParams& p, hipStream_t s);
+// launch_bwd_cols: a launch of the column forms' kernel: p.col_tasks column
+// tasks, then (with rows) p.chunks row tasks.
+hipError_t launch_bwd_cols(int layout, bool w_f32, const BwdParams& p, bool rows, hipStream_t s);
 hipError_t launch_dw_reduce(const double* part, int chunks, int H, float* dw, hipStream_t s);
 hipError_t launch_fill_zero(void* ptr, int64_t bytes, hipStream_t s);
+
 
 }  // namespace rmsn

@@ -11,58 +11,116 @@
 
 namespace rmsn {
 
-int bwd_direct_rows_per_iter(int64_t H)
-{
-    const int id = pick_layout(kBwdLayouts, kNumBwdLayouts, H);
-    if (id < 0) return 0;
-    const Layout& L = kBwdLayouts[id];
-    return slots_of(L.lpr) * direct_max_u(L.lpr, L.v, L.u);
-}
-
 size_t ws_bytes_for(int64_t R, int64_t H, const BwdRoute& r)
 {
     size_t b = ws_part_offset(H);
     (void)R;
     if (r.form == FORM_PAIR && r.chunks > 1) b += (size_t)r.chunks * (size_t)H * 8;
+    if ((r.form == FORM_COLS || r.form == FORM_COLS_TICKET) && r.col_chunks > 1)
+        b += (size_t)r.col_chunks * (size_t)H * 8;
     return b;
+}
+
+bool route_valid(const BwdRoute& r, bool deterministic)
+{
+    if (r.chunks < 1 || r.chunks > kMaxChunks) return false;
+    switch (r.form) {
+    case FORM_PAIR:
+        return r.col_chunks == 0 && r.col_vecs == 0;
+    case FORM_ATOMIC:
+        return !deterministic && r.col_chunks == 0 && r.col_vecs == 0;
+    case FORM_COLS:
+    case FORM_COLS_TICKET: {
+        if (r.form == FORM_COLS_TICKET && (deterministic || r.col_chunks < 2)) return false;
+        const int v = r.col_vecs;
+        return r.col_chunks >= 1 && r.col_chunks <= kMaxColChunks && (v == 1 || v == 2 || v == 4 || v == 8);
+    }
+    default:
+        return false;
+    }
+}
+
+// Column forms (measured on MI355X, cold caches, BF16 w, H 256-8192, R 16 to
+// 16384; per-head views [T,4,256] too).  The one-pass form -- dw written by
+// column tasks that each read all rows of an 8 * col_vecs-column slice, one
+// launch, no workspace -- beats the pair at every width up to R = 384 (H <=
+// 3072), 512 (H <= 6144) and 1024 (wider rows): H 4096, R 16: 6.2 against
+// 10.7 us; R 256: 8.2 against 12.2 us; H 6144, R 512: 13.0 against 18.8 us
+// (HIP events around a one-element fill read 6.0 us on the same machine).
+// Its slice width: about one batch of four rows per column-task lane at
+// R <= 128 (8 vectors); above that wider rows, having more slices, keep
+// wider slices (fewer, longer column tasks):
+static int cols1_vecs(int64_t R, int64_t H)
+{
+    if (R <= 128 || H > 6144) return 8;
+    if (R <= 256) return 4;
+    if (R <= 512) return H <= 4096 ? 2 : 4;
+    return H <= 1024 ? 1 : 2;
+}
+
+static int64_t cols1_max_rows(int64_t H) { return H <= 3072 ? 384 : (H <= 6144 ? 512 : 1024); }
+
+// Beyond that the two-launch column form -- 8-vector slices cut into
+// col_chunks row blocks whose partials the reduce kernel sums, about 192
+// column tasks in all (col_chunks ~ 12288 / H) -- beats the pair up to about
+// R * H = 3.2 M elements at H <= 2048 (H 1536, R 2048: 13.5 against 16.2 us),
+// 4.8 M at H 3072 and 6.4 M up to H 6144 (H 4096, R 1536: 20.8 against 21.8
+// us; H 6144, R 1024: 21.2 against 22.8 us); past those the pair, whose rows
+// are read once, wins (H 4096, R 4096: 32.3 against 41.5 us).
+static int64_t cols_max_elems(int64_t H)
+{
+    if (H <= 2048) return 3200000;
+    if (H <= 3072) return 4800000;
+    if (H <= 6144) return 6400000;
+    return 8400000;
+}
+
+// The fixed-order pair's chunking for R rows of width H.
+BwdRoute pair_route(int64_t R, int64_t H)
+{
+    const int id = pick_layout(kBwdLayouts, kNumBwdLayouts, H);
+    const Layout& L = kBwdLayouts[id < 0 ? 0 : id];
+    const int64_t rpi = (int64_t)slots_of(L.lpr) * L.u;
+    const int64_t groups = (R + rpi - 1) / rpi;
+    // Measured on MI355X with cold caches, T*H from 2^23 to 2^30 elements,
+    // both weight dtypes: the layout's chunk count (512 -- two workgroups per
+    // compute unit -- for H <= 6144, 256 above) beats the other counts by
+    // 4-20 %, and the fixed-order pair beats the atomic form at every shape
+    // (FP64 atomics from hundreds of workgroups to the same H addresses
+    // serialise).
+    // Below that size each workgroup should still get about four rows: the
+    // chunk partials (chunks * H * 8 bytes, written and read back) would
+    // otherwise cost more than the rows themselves.  Measured at H 1536 to
+    // 6144, T 256 to 2048: 4 rows per workgroup, but never fewer than 128
+    // workgroups, is best or within 1.4 us of the best count.
+    const int64_t per = (4 + rpi - 1) / rpi;  // row groups per workgroup
+    int64_t c = (groups + per - 1) / per;
+    if (c < 128) c = groups < 128 ? groups : 128;
+    if (c > L.k) c = L.k;
+    return BwdRoute{FORM_PAIR, (int)(c > 0 ? c : 1), 0, 0};
 }
 
 BwdRoute default_bwd_route(int64_t R, int64_t H, bool w_f32, bool residual, bool deterministic)
 {
     (void)w_f32;
     (void)residual;
-    (void)deterministic;
+    (void)deterministic;  // every routed form is deterministic: both modes take the same route
     const int id = pick_layout(kBwdLayouts, kNumBwdLayouts, H);
     const Layout& L = kBwdLayouts[id < 0 ? 0 : id];
-    const int64_t rpi = (int64_t)slots_of(L.lpr) * L.u;
-    const int64_t groups = (R + rpi - 1) / rpi;
-    BwdRoute r;
-    // Measured on MI355X with cold caches, T*H from 2^23 to 2^30 elements,
-    // both weight dtypes: the layout's chunk count (512 -- two workgroups per
-    // compute unit -- for H <= 6144, 256 above) beats the other counts by
-    // 4-20 %, and the fixed-order pair beats the atomic form at every shape
-    // (FP64 atomics from hundreds of workgroups to the same H addresses
-    // serialise), so both modes take the pair.
-    r.form = FORM_PAIR;
-    // Below that size each workgroup should still get about four rows: the
-    // chunk partials (chunks * H * 8 bytes, written and read back) would
-    // otherwise cost more than the rows themselves.  Measured at H 1536 to
-    // 6144, T 256 to 2048: 4 rows per workgroup, but never fewer than 128
-    // workgroups, is best or within 1.4 us of the best count, and 1.5-3 us
-    // faster than one row group per workgroup at T 256 to 1024.
-    const int64_t per = (4 + rpi - 1) / rpi;  // row groups per workgroup
-    int64_t c = (groups + per - 1) / per;
-    if (c < 128) c = groups < 128 ? groups : 128;
-    if (c > L.k) c = L.k;
-    r.chunks = (int)(c > 0 ? c : 1);
-    // When one iteration of a single workgroup covers every row (it may take
-    // more rows per iteration than the multi-workgroup layout, see
-    // direct_max_u), that workgroup writes dw itself and the reduce launch
-    // goes: measured at T 1-128, H 256-6144, 0.5-2 us faster than the pair
-    // with one row group per workgroup; one more iteration already costs
-    // 1.3-4 us (cold loads in series), more than the reduce launch.
-    if (groups <= 2 || R <= (int64_t)bwd_direct_rows_per_iter(H)) r.chunks = 1;
-    return r;
+    // column forms: row tasks take one row per row group, so a row group is
+    // slots_of(lpr) rows there
+    const int64_t cgroups = (R + slots_of(L.lpr) - 1) / slots_of(L.lpr);
+    if (R <= cols1_max_rows(H)) {
+        const int64_t c = cgroups < 1 ? 1 : cgroups;
+        return BwdRoute{FORM_COLS, (int)c, 1, cols1_vecs(R, H)};
+    }
+    if (R * H <= cols_max_elems(H)) {
+        const int64_t c = cgroups < 512 ? cgroups : 512;
+        int64_t cc = (12288 + H / 2) / H;
+        if (cc < 2) cc = 2;
+        return BwdRoute{FORM_COLS, (int)c, (int)cc, 8};
+    }
+    return pair_route(R, H);
 }
 
 }  // namespace rmsn

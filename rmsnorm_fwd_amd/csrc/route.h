@@ -9,32 +9,63 @@
 
 namespace rmsn {
 
-// pair: FP64 partials + fixed-order reduce kernel (with one chunk the row
-// kernel writes dw itself); atomic: FP64 atomic adds, last workgroup writes dw.
-enum { FORM_PAIR = 0, FORM_ATOMIC = 1 };
+// How the backward forms dw (the column sum over all rows):
+//   FORM_PAIR    row kernel writes one FP64 partial row per chunk of rows, a
+//                second kernel sums them in a fixed order (with one chunk the
+//                row kernel writes dw itself and there is no second kernel);
+//   FORM_ATOMIC  row kernel adds its chunk partials into an FP64 accumulator
+//                atomically, the last workgroup to finish writes dw;
+//   FORM_COLS    one launch of two kinds of workgroups: row tasks form dx
+//                only; column tasks form dw for a slice of columns straight
+//                from u, dy and rstd, in a fixed order.  With col_chunks > 1
+//                each slice's rows are cut into col_chunks blocks whose FP64
+//                partials the fixed-order reduce kernel sums (a second
+//                launch, but over col_chunks rows instead of one per chunk);
+//   FORM_COLS_TICKET  FORM_COLS with col_chunks > 1, where the column task
+//                that finishes a slice last (a per-slice arrival ticket) sums
+//                that slice's partials in the fixed order: one launch.
+enum { FORM_PAIR = 0, FORM_ATOMIC = 1, FORM_COLS = 2, FORM_COLS_TICKET = 3 };
 
 struct BwdRoute {
-    int form;    // FORM_PAIR or FORM_ATOMIC
-    int chunks;  // workgroups of the row kernel (= FP64 partial rows of the pair form)
+    int form;        // FORM_*
+    int chunks;      // workgroups that walk the rows (row kernel, or row tasks of the column forms)
+    int col_chunks;  // column forms: row blocks per column slice (1: one pass over all rows)
+    int col_vecs;    // column forms: 16-byte vectors (8 columns each) per column slice: 1, 2, 4 or 8
 };
 
-// Workspace layout: [0, 256) header (arrival ticket at offset 0),
-// [256, 256 + pad256(8H)) FP64 accumulator for the atomic form,
-// then chunks * H FP64 partials for the pair form.
+// Workspace layout (bytes, every part 256-aligned):
+//   [0, 256)                  header: the arrival ticket of the atomic form at offset 0
+//   [256, +pad256(8H))        FP64 [H] accumulator of the atomic form
+//   [.., +pad256(4*ceil(H/8))) per-slice arrival tickets of FORM_COLS_TICKET
+//   [ws_part_offset(H), ...)  FP64 partials: chunks x H (pair), col_chunks x H (column forms)
+// Everything before ws_part_offset is the "prepared" part: zero before the
+// first non-deterministic call and left zero by every call.
 constexpr size_t kWsHeader = 256;
 inline size_t pad256(size_t b) { return (b + 255) & ~(size_t)255; }
 inline size_t ws_acc_offset() { return kWsHeader; }
-inline size_t ws_part_offset(int64_t H) { return kWsHeader + pad256((size_t)H * 8); }
+inline size_t ws_slice_ticket_offset(int64_t H) { return kWsHeader + pad256((size_t)H * 8); }
+inline size_t ws_part_offset(int64_t H)
+{
+    return ws_slice_ticket_offset(H) + pad256((size_t)((H + 7) / 8) * sizeof(unsigned));
+}
 size_t ws_bytes_for(int64_t R, int64_t H, const BwdRoute& r);
+
+// Column slices of a column form: ceil(H / (8 * col_vecs)).
+inline int64_t col_slices(int64_t H, int col_vecs) { return (H + 8 * col_vecs - 1) / (8 * col_vecs); }
 
 // The measured route table (route.cpp).
 BwdRoute default_bwd_route(int64_t R, int64_t H, bool w_f32, bool residual, bool deterministic);
 
-// Rows one iteration covers when a single workgroup does every row (chunks
-// = 1, dw written directly) for this width.
-int bwd_direct_rows_per_iter(int64_t H);
+// The pair's chunking alone.
+BwdRoute pair_route(int64_t R, int64_t H);
 
-// Largest chunk count a route may ask for.
+// Largest chunk count a route may ask for, and largest row-block count per
+// column slice.
 constexpr int64_t kMaxChunks = 1 << 16;
+constexpr int64_t kMaxColChunks = 1 << 12;
+
+// Whether a route is well formed for this mode (host validation of the route
+// override): the atomic and ticket forms only without determinism.
+bool route_valid(const BwdRoute& r, bool deterministic);
 
 }  // namespace rmsn

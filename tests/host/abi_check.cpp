@@ -9,6 +9,9 @@
 //   * for a sweep of shapes, the backward's workspace accesses (ticket,
 //     FP64 accumulator, chunk partials) stay inside rmsnorm_bwd_workspace_size,
 //     one byte less is refused, and the launch parameters are in range;
+//   * the same for explicit column-form routes (slice tickets inside the
+//     prepared part, row-block partials inside the workspace, the reduce
+//     launched exactly for the deterministic multi-block form);
 //   * the forward grid is within [1, compute units * layout cap] and every
 //     launch gets the row count and width it was given.
 // Prints "ok" and exits 0, or prints the first failures and exits 1.
@@ -25,7 +28,7 @@
 namespace rmsn {
 
 struct Calls {
-    int fwd = 0, bwd = 0, reduce = 0, fill = 0;
+    int fwd = 0, bwd = 0, cols = 0, cols_rows = 0, cols_col_tasks = 0, reduce = 0, fill = 0;
     FwdParams fp{};
     BwdParams bp{};
     int grid = 0, layout = -1, fwd_table = -1, reduce_chunks = 0, reduce_h = 0;
@@ -46,6 +49,15 @@ hipError_t launch_fwd(int table, int layout, bool, const FwdParams& p, int grid,
 hipError_t launch_bwd(int layout, bool, const BwdParams& p, hipStream_t)
 {
     ++g.bwd;
+    g.bp = p;
+    g.layout = layout;
+    return hipSuccess;
+}
+hipError_t launch_bwd_cols(int layout, bool, const BwdParams& p, bool rows, hipStream_t)
+{
+    ++g.cols;
+    g.cols_rows += rows ? 1 : 0;
+    g.cols_col_tasks += p.col_tasks;
     g.bp = p;
     g.layout = layout;
     return hipSuccess;
@@ -153,9 +165,12 @@ static void check_error_paths()
     CHECK(g.fwd == 0, "a rejected forward launched");
 
     // backward
-    const size_t ws = rmsnorm_bwd_workspace_size(64, 1, H, 1);
+    const size_t ws = rmsnorm_bwd_workspace_size(64, 1, H, RMSN_W_F32, nullptr, 1);
+    rmsn_route rt64{};
+    CHECK(rmsnorm_bwd_route(64, 1, H, RMSN_W_F32, 0, 1, &rt64) == RMSN_OK, "route query");
     reset();
-    CHECK(bwd(64, 1, H, ws - 1, 1) == RMSN_ERR_WORKSPACE, "workspace one byte short");
+    CHECK(bwd(64, 1, H, rmsnorm_bwd_workspace_size_for_route(64, 1, H, rt64) - 1, 1) == RMSN_ERR_WORKSPACE,
+          "workspace one byte short");
     CHECK(rmsnorm_bwd(P(0), P(1), (const float*)P(2), P(3), RMSN_W_F32, nullptr, P(4), (float*)P(5),
                       (char*)P(6) + 128, ws, 64, 1, H, H, H, 1, nullptr) == RMSN_ERR_MISALIGNED,
           "workspace misaligned");
@@ -165,15 +180,19 @@ static void check_error_paths()
                       P(6), ws, 64, 1, H, H, H, 1, nullptr) == RMSN_ERR_MISALIGNED, "rstd misaligned");
     CHECK(rmsnorm_bwd(P(0), P(1), (const float*)P(2), P(3), RMSN_W_F32, (char*)P(7) + 8, P(4), (float*)P(5), P(6),
                       ws, 64, 1, H, H, H, 1, nullptr) == RMSN_ERR_MISALIGNED, "dres misaligned");
-    const rmsn_route atomic{RMSN_FORM_ATOMIC, 8}, zero{RMSN_FORM_PAIR, 0}, many{RMSN_FORM_PAIR, 65537},
-        bad_form{7, 8};
-    for (const rmsn_route& r : {zero, many, bad_form})
+    const rmsn_route atomic{RMSN_FORM_ATOMIC, 8, 0, 0}, zero{RMSN_FORM_PAIR, 0, 0, 0},
+        many{RMSN_FORM_PAIR, 65537, 0, 0}, bad_form{7, 8, 0, 0}, pair_cols{RMSN_FORM_PAIR, 8, 1, 8},
+        cols_zero{RMSN_FORM_COLS, 8, 0, 8}, cols_many{RMSN_FORM_COLS, 8, 4097, 8}, cols_v3{RMSN_FORM_COLS, 8, 1, 3},
+        cols_v16{RMSN_FORM_COLS, 8, 1, 16}, ticket_one{RMSN_FORM_COLS_TICKET, 8, 1, 8},
+        ticket{RMSN_FORM_COLS_TICKET, 8, 4, 8};
+    for (const rmsn_route& r : {zero, many, bad_form, pair_cols, cols_zero, cols_many, cols_v3, cols_v16, ticket_one})
         CHECK(rmsnorm_bwd_routed(P(0), P(1), (const float*)P(2), P(3), RMSN_W_F32, nullptr, P(4), (float*)P(5), P(6),
                                  ws, 64, 1, H, H, H, 0, r, nullptr) == RMSN_ERR_INVALID_ARG,
-              "route (%d, %d)", r.form, r.chunks);
-    CHECK(rmsnorm_bwd_routed(P(0), P(1), (const float*)P(2), P(3), RMSN_W_F32, nullptr, P(4), (float*)P(5), P(6), ws,
-                             64, 1, H, H, H, 1, atomic, nullptr) == RMSN_ERR_INVALID_ARG,
-          "deterministic atomic route");
+              "route (%d, %d, %d, %d)", r.form, r.chunks, r.col_chunks, r.col_vecs);
+    for (const rmsn_route& r : {atomic, ticket})
+        CHECK(rmsnorm_bwd_routed(P(0), P(1), (const float*)P(2), P(3), RMSN_W_F32, nullptr, P(4), (float*)P(5), P(6),
+                                 ws, 64, 1, H, H, H, 1, r, nullptr) == RMSN_ERR_INVALID_ARG,
+              "deterministic route of form %d", r.form);
     CHECK(rmsnorm_gated_bwd(P(0), P(1), nullptr, (const float*)P(2), P(3), RMSN_W_F32, P(4), P(7), (float*)P(5),
                             P(6), ws, 64, 1, H, H, H, 1, nullptr) == RMSN_ERR_INVALID_ARG, "gate null");
     CHECK(rmsnorm_gated_bwd(P(0), P(1), P(8), (const float*)P(2), P(3), RMSN_W_F32, P(4), (char*)P(7) + 4,
@@ -181,10 +200,12 @@ static void check_error_paths()
           "dgate misaligned");
     CHECK(rmsnorm_bwd_workspace_init(P(6), ws, 12, nullptr) == RMSN_ERR_INVALID_ARG, "init H = 12");
     CHECK(rmsnorm_bwd_workspace_init(P(6), 100, H, nullptr) == RMSN_ERR_WORKSPACE, "init too small");
-    CHECK(g.bwd == 0 && g.reduce == 0 && g.fill == 0, "a rejected backward launched");
-    CHECK(rmsnorm_bwd_workspace_size(4, 1, 12, 1) == 0 && rmsnorm_bwd_workspace_size(-1, 1, H, 1) == 0 &&
-              rmsnorm_bwd_workspace_size(int64_t(1) << 30, 1, H, 1) == 0,
-          "workspace size of an invalid shape is not 0");
+    CHECK(g.bwd == 0 && g.cols == 0 && g.reduce == 0 && g.fill == 0, "a rejected backward launched");
+    CHECK(rmsnorm_bwd_workspace_size(4, 1, 12, RMSN_W_BF16, nullptr, 1) == 0 &&
+              rmsnorm_bwd_workspace_size(-1, 1, H, RMSN_W_BF16, nullptr, 1) == 0 &&
+              rmsnorm_bwd_workspace_size(int64_t(1) << 30, 1, H, RMSN_W_BF16, nullptr, 1) == 0 &&
+              rmsnorm_bwd_workspace_size(4, 1, H, 2, nullptr, 1) == 0,
+          "workspace size of an invalid shape or dtype is not 0");
 
     // R = 0: the backward zero-fills dw and launches nothing else
     reset();
@@ -197,43 +218,119 @@ static void check_error_paths()
     for (int s = -1; s <= 6; ++s) CHECK(rmsnorm_status_string(s) != nullptr, "status string %d", s);
 }
 
-// One backward call at (T, heads, H) in both modes: bounds of every
-// workspace access, launch parameters, and the one-byte-short refusal.
+// Where the workspace accesses of the launch just recorded fall, for a
+// workspace of ws bytes at `base`: every one inside it.
+static void check_ws_accesses(const char* base, size_t ws, int64_t H, int form, const char* what)
+{
+    const BwdParams& p = g.bp;
+    CHECK((const char*)p.ticket == base && (const char*)p.acc >= base + sizeof(unsigned),
+          "%s: ticket/accumulator placement", what);
+    CHECK((size_t)((const char*)p.acc - base) + (size_t)H * 8 <= (size_t)((const char*)p.slice_ticket - base),
+          "%s: accumulator runs into the slice tickets", what);
+    CHECK((size_t)((const char*)p.acc - base) % 8 == 0 && (size_t)((const char*)p.part - base) % 16 == 0 &&
+              (size_t)((const char*)p.slice_ticket - base) % 4 == 0,
+          "%s: workspace alignment", what);
+    CHECK((size_t)((const char*)p.part - base) <= ws, "%s: partials start past the workspace", what);
+    if (form == FORM_PAIR && p.chunks > 1)
+        CHECK((size_t)((const char*)p.part - base) + (size_t)p.chunks * H * 8 <= ws,
+              "%s: pair partials past the workspace (chunks %d)", what, p.chunks);
+    if (form == FORM_COLS || form == FORM_COLS_TICKET) {
+        CHECK(p.slices == (int)col_slices(H, p.col_vecs) && (int64_t)p.slices * p.col_vecs * 8 >= H &&
+                  (int64_t)(p.slices - 1) * p.col_vecs * 8 < H,
+              "%s: slices %d for H %lld", what, p.slices, (long long)H);
+        CHECK((size_t)((const char*)p.slice_ticket - base) + (size_t)p.slices * sizeof(unsigned) <=
+                  (size_t)((const char*)p.part - base),
+              "%s: slice tickets run into the partials", what);
+        if (p.col_chunks > 1)
+            CHECK((size_t)((const char*)p.part - base) + (size_t)p.col_chunks * H * 8 <= ws,
+                  "%s: row-block partials past the workspace (col_chunks %d)", what, p.col_chunks);
+    }
+}
+
+// One backward call at (T, heads, H) in both modes, both weight dtypes,
+// with and without dres: bounds of every workspace access, launch
+// parameters, and the one-byte-short refusal.
 static void check_backward_shape(int64_t T, int64_t heads, int64_t H)
 {
     const int64_t R = T * heads;
-    for (int det = 0; det <= 1; ++det) {
-        const size_t ws = rmsnorm_bwd_workspace_size(T, heads, H, det);
-        CHECK(ws > 0, "workspace size 0 for T=%lld heads=%lld H=%lld", (long long)T, (long long)heads, (long long)H);
-        reset();
-        const int st = bwd(T, heads, H, ws, det);
-        CHECK(st == RMSN_OK, "status %d for T=%lld heads=%lld H=%lld", st, (long long)T, (long long)heads,
-              (long long)H);
-        if (st != RMSN_OK || R == 0) continue;
-        const BwdParams& p = g.bp;
-        const char* base = (const char*)P(6);
-        CHECK(g.bwd == 1 && p.R == R && p.H == H, "launch R/H");
-        CHECK(p.chunks >= 1 && p.chunks <= kMaxChunks, "chunks %d", p.chunks);
-        CHECK(p.form == FORM_PAIR, "default route is the pair");
-        CHECK((const char*)p.ticket == base && (const char*)p.acc >= base + sizeof(unsigned),
-              "ticket/accumulator placement");
-        CHECK((size_t)((const char*)p.acc - base) + (size_t)H * 8 <= ws, "accumulator past the workspace");
-        CHECK((size_t)((const char*)p.acc - base) % 8 == 0 && (size_t)((const char*)p.part - base) % 16 == 0,
-              "workspace alignment");
-        if (p.chunks > 1) {
-            CHECK(!p.direct_dw && g.reduce == 1 && g.reduce_chunks == p.chunks && g.reduce_h == H,
-                  "pair launches its reduce");
-            CHECK((size_t)((const char*)p.part - base) + (size_t)p.chunks * H * 8 <= ws,
-                  "partials past the workspace: T=%lld heads=%lld H=%lld chunks=%d", (long long)T,
-                  (long long)heads, (long long)H, p.chunks);
-        } else {
-            CHECK(p.direct_dw && g.reduce == 0, "one chunk writes dw itself");
-        }
-        const size_t need = ws_bytes_for(R, H, BwdRoute{p.form, p.chunks});
-        reset();
-        CHECK(bwd(T, heads, H, need - 1, det) == RMSN_ERR_WORKSPACE && g.bwd == 0,
-              "a workspace one byte short is refused");
-    }
+    for (int det = 0; det <= 1; ++det)
+        for (int wd = 0; wd <= 1; ++wd)
+            for (int res = 0; res <= 1; ++res) {
+                const void* dres = res ? P(7) : nullptr;
+                const size_t ws = rmsnorm_bwd_workspace_size(T, heads, H, wd, dres, det);
+                CHECK(ws > 0, "workspace size 0 for T=%lld heads=%lld H=%lld", (long long)T, (long long)heads,
+                      (long long)H);
+                rmsn_route rt{};
+                CHECK(rmsnorm_bwd_route(T, heads, H, wd, res, det, &rt) == RMSN_OK, "route query");
+                CHECK(ws == rmsnorm_bwd_workspace_size_for_route(T, heads, H, rt), "size of the route");
+                CHECK(!det || rt.form == RMSN_FORM_PAIR || rt.form == RMSN_FORM_COLS, "deterministic route form");
+                reset();
+                const int64_t sh = H, st = heads * sh;
+                const int st_ = rmsnorm_bwd(P(0), P(1), (const float*)P(2), P(3), wd, dres, P(4), (float*)P(5), P(6),
+                                            ws, T, heads, H, st, sh, det, nullptr);
+                CHECK(st_ == RMSN_OK, "status %d for T=%lld heads=%lld H=%lld", st_, (long long)T, (long long)heads,
+                      (long long)H);
+                if (st_ != RMSN_OK || R == 0) continue;
+                const BwdParams& p = g.bp;
+                CHECK(g.bwd + g.cols == 1 && p.R == R && p.H == H, "launch R/H");
+                CHECK(g.cols == 0 || (g.cols_rows == 1 && p.col_tasks == p.slices * p.col_chunks),
+                      "one column-form launch holds the column and the row tasks");
+                CHECK(p.chunks >= 1 && p.chunks <= kMaxChunks, "chunks %d", p.chunks);
+                CHECK(p.form == rt.form && p.chunks == rt.chunks, "launch follows the route");
+                check_ws_accesses((const char*)P(6), ws, H, p.form, "rmsnorm_bwd");
+                if (p.form == FORM_PAIR && p.chunks > 1)
+                    CHECK(!p.direct_dw && g.reduce == 1 && g.reduce_chunks == p.chunks && g.reduce_h == H,
+                          "pair launches its reduce");
+                if (p.form == FORM_PAIR && p.chunks == 1) CHECK(p.direct_dw && g.reduce == 0, "one chunk writes dw");
+                reset();
+                const size_t need = rmsnorm_bwd_workspace_size_for_route(T, heads, H, rt);
+                CHECK(rmsnorm_bwd(P(0), P(1), (const float*)P(2), P(3), wd, dres, P(4), (float*)P(5), P(6), need - 1,
+                                  T, heads, H, st, sh, det, nullptr) == RMSN_ERR_WORKSPACE &&
+                          g.bwd + g.cols == 0,
+                      "a workspace one byte short of the route's is refused");
+                // in place (dx = dy): the same route; a column form runs its
+                // column tasks alone, then its row tasks alone
+                reset();
+                CHECK(rmsnorm_bwd(P(0), P(1), (const float*)P(2), P(3), wd, dres, P(0), (float*)P(5), P(6), ws, T,
+                                  heads, H, st, sh, det, nullptr) == RMSN_OK && g.bp.form == rt.form,
+                      "an in-place backward");
+                if (rt.form == RMSN_FORM_COLS)
+                    CHECK(g.cols == 2 && g.cols_rows == 1 && g.bp.col_tasks == 0 &&
+                              g.cols_col_tasks == (int)col_slices(H, rt.col_vecs) * rt.col_chunks,
+                          "in place, the column tasks run before the row tasks, in launches of their own");
+                else
+                    CHECK(g.bwd == 1 && g.cols == 0, "in place, the row kernel");
+                check_ws_accesses((const char*)P(6), ws, H, rt.form, "in place");
+            }
+}
+
+// Explicit column-form routes: launch parameters and workspace bounds.
+static void check_column_routes(int64_t T, int64_t H)
+{
+    for (int form : {RMSN_FORM_COLS, RMSN_FORM_COLS_TICKET})
+        for (int vecs : {1, 2, 4, 8})
+            for (int cc : {1, 2, 3, 16, 4096}) {
+                if (form == RMSN_FORM_COLS_TICKET && cc < 2) continue;
+                const rmsn_route r{form, 37, cc, vecs};
+                const size_t ws = rmsnorm_bwd_workspace_size_for_route(T, 1, H, r);
+                CHECK(ws >= ws_part_offset(H), "column route workspace");
+                reset();
+                const int det = form == RMSN_FORM_COLS;
+                const int st = rmsnorm_bwd_routed(P(0), P(1), (const float*)P(2), P(3), RMSN_W_BF16, nullptr, P(4),
+                                                  (float*)P(5), P(6), ws, T, 1, H, H, H, det, r, nullptr);
+                CHECK(st == RMSN_OK, "column route status %d", st);
+                if (st != RMSN_OK || T == 0) continue;
+                CHECK(g.cols == 1 && g.bwd == 0 && g.bp.col_chunks == cc && g.bp.col_vecs == vecs && g.bp.chunks == 37,
+                      "column launch parameters");
+                CHECK(g.reduce == (form == RMSN_FORM_COLS && cc > 1 ? 1 : 0) && (g.reduce == 0 || g.reduce_chunks == cc),
+                      "reduce launch of the column form");
+                check_ws_accesses((const char*)P(6), ws, H, form, "column route");
+                reset();
+                CHECK(rmsnorm_bwd_routed(P(0), P(1), (const float*)P(2), P(3), RMSN_W_BF16, nullptr, P(4),
+                                         (float*)P(5), P(6), ws - 1, T, 1, H, H, H, det, r, nullptr) ==
+                          RMSN_ERR_WORKSPACE,
+                      "column route one byte short");
+            }
 }
 
 static void check_forward_shape(int64_t T, int64_t heads, int64_t H, bool residual)
@@ -275,6 +372,8 @@ int main()
     check_gated_forward_table();
     const int64_t Ts[] = {1, 2, 3, 4, 5, 7, 16, 63, 64, 65, 255, 256, 257, 1000, 1024, 4096, 4099,
                           16384, 32767, 32768, 65535, 65536, 131072, 1 << 20, (int64_t(1) << 30) - 1};
+    for (int64_t H : {int64_t(8), int64_t(64), int64_t(72), int64_t(1536), int64_t(6144), int64_t(16384)})
+        for (int64_t T : {int64_t(1), int64_t(5), int64_t(4099)}) check_column_routes(T, H);
     for (int64_t H = 8; H <= RMSN_MAX_H; H += (H < 1024 ? 8 : (H < 8192 ? 72 : 520))) {
         for (int64_t T : Ts) {
             check_backward_shape(T, 1, H);

@@ -9,6 +9,7 @@ import subprocess
 import pytest
 
 import rmsnorm_fwd_amd as rn
+from tests.helpers import prepared_bytes
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "rmsnorm.h")
@@ -106,23 +107,29 @@ def test_bwd_rejects_bad_arguments(kw, status):
     assert _bwd(**kw) == status
 
 
-def test_workspace_size_is_pure_and_covers_both_modes():
+def test_workspace_size_follows_the_route():
+    # the size is that of the route rmsnorm_bwd takes for the same arguments,
+    # a pure function of them, never below the prepared part, and 0 for
+    # invalid shapes or weight dtypes
     for (T, heads, H) in [(4096, 1, 1536), (65536, 1, 4096), (131072, 1, 6144), (32768, 24, 256),
-                          (1, 1, 8), (0, 1, 64)]:
-        a = rn.rmsnorm_bwd_workspace_size(T, heads, H, True)
-        b = rn.rmsnorm_bwd_workspace_size(T, heads, H, False)
-        assert a == b == rn.rmsnorm_bwd_workspace_size(T, heads, H, True)
-        assert a > 0 and a % 256 == 0 or a > 0
+                          (1, 1, 8), (0, 1, 64), (64, 1, 4096), (777, 1, 2048)]:
         for det in (0, 1):
             for wd in (0, 1):
                 for res in (0, 1):
+                    a = rn.rmsnorm_bwd_workspace_size(T, heads, H, wd, res, det)
+                    assert a == rn.rmsnorm_bwd_workspace_size(T, heads, H, wd, res, det)
                     route = rn.rmsnorm_bwd_route(T, heads, H, wd, res, det)
-                    need = rn.rmsnorm_bwd_workspace_size_for_route(T, heads, H, route)
-                    assert 0 < need <= a
+                    assert a == rn.rmsnorm_bwd_workspace_size_for_route(T, heads, H, route) > 0
+                    assert a >= prepared_bytes(H)
                     if det:
-                        assert route[0] == rn.RMSN_FORM_PAIR
-    assert rn.rmsnorm_bwd_workspace_size(10, 1, 12, True) == 0
-    assert rn.rmsnorm_bwd_workspace_size(-1, 1, 64, True) == 0
+                        assert route[0] in (rn.RMSN_FORM_PAIR, rn.RMSN_FORM_COLS)
+    assert rn.rmsnorm_bwd_workspace_size(10, 1, 12) == 0
+    assert rn.rmsnorm_bwd_workspace_size(-1, 1, 64) == 0
+    assert rn.rmsnorm_bwd_workspace_size(10, 1, 64, w_dtype=2) == 0
+    # the binding's workspace helper serves both modes with one allocation
+    for (T, H) in [(64, 4096), (65536, 4096)]:
+        both = max(rn.rmsnorm_bwd_workspace_size(T, 1, H, 0, False, d) for d in (0, 1))
+        assert both == max(rn.rmsnorm_bwd_workspace_size(T, 1, H, deterministic=d) for d in (True, False))
 
 
 def test_route_chunks_depend_only_on_shape():
@@ -133,13 +140,27 @@ def test_route_chunks_depend_only_on_shape():
     assert r1 == r2 and r1[1] >= 1
 
 
-def test_routed_rejects_atomic_form_in_deterministic_mode():
-    st = rn.lib().rmsnorm_bwd_routed(GOOD, GOOD, GOOD, GOOD, 0, None, GOOD, GOOD, GOOD, 1 << 30,
-                                     4, 1, 64, 64, 64, 1, rn.RmsnRoute(rn.RMSN_FORM_ATOMIC, 4), None)
-    assert st == rn.RMSN_ERR_INVALID_ARG
-    st = rn.lib().rmsnorm_bwd_routed(GOOD, GOOD, GOOD, GOOD, 0, None, GOOD, GOOD, GOOD, 1 << 30,
-                                     4, 1, 64, 64, 64, 0, rn.RmsnRoute(rn.RMSN_FORM_PAIR, 0), None)
-    assert st == rn.RMSN_ERR_INVALID_ARG
+def _routed(route, det=1, T=4, H=64):
+    return rn.lib().rmsnorm_bwd_routed(GOOD, GOOD, GOOD, GOOD, 0, None, GOOD, GOOD, GOOD, 1 << 30,
+                                       T, 1, H, H, H, det, rn.RmsnRoute(*route), None)
+
+
+@pytest.mark.parametrize("route,det", [
+    ((rn.RMSN_FORM_ATOMIC, 4), 1),              # atomic accumulation is not deterministic
+    ((rn.RMSN_FORM_PAIR, 0), 0),                # no workgroups
+    ((rn.RMSN_FORM_PAIR, 65537), 0),            # too many
+    ((7, 8), 0),                                # no such form
+    ((rn.RMSN_FORM_PAIR, 8, 1, 8), 0),          # column fields on a row form
+    ((rn.RMSN_FORM_COLS, 8, 0, 8), 1),          # no row blocks
+    ((rn.RMSN_FORM_COLS, 8, 4097, 8), 1),       # too many row blocks
+    ((rn.RMSN_FORM_COLS, 8, 1, 3), 1),          # slice width not a power of two
+    ((rn.RMSN_FORM_COLS, 8, 1, 16), 1),         # slice wider than 8 vectors
+    ((rn.RMSN_FORM_COLS_TICKET, 8, 4, 8), 1),   # tickets need the prepared workspace
+    ((rn.RMSN_FORM_COLS_TICKET, 8, 1, 8), 0),   # a ticket needs two row blocks at least
+])
+def test_routed_rejects_malformed_routes(route, det):
+    assert _routed(route, det) == rn.RMSN_ERR_INVALID_ARG
+    assert rn.rmsnorm_bwd_workspace_size_for_route(4, 1, 64, route) == 0 or det
 
 
 def test_status_strings():
@@ -189,18 +210,27 @@ def test_oracle_under_sanitizers(tmp_path):
     assert out.returncode == 0 and out.stdout.strip().endswith("ok"), out.stdout + out.stderr
 
 
-def test_route_chunk_count_grows_with_rows_and_stays_bounded():
-    # one workgroup per chunk: never more than 512 (two per compute unit), one
-    # for the smallest inputs, and never fewer as the row count grows
-    for H in (256, 1536, 4096, 5120, 6144, 16384):
+def test_route_table_moves_from_column_forms_to_the_pair():
+    # as rows grow: the one-pass column form (one launch, no partials), then
+    # the two-launch column form, then the fixed-order pair; never back.  Both
+    # modes take the same route (every routed form is deterministic); chunk
+    # counts stay within their bounds
+    order = {(rn.RMSN_FORM_COLS, True): 0, (rn.RMSN_FORM_COLS, False): 1, (rn.RMSN_FORM_PAIR, False): 2}
+    for H in (256, 512, 1536, 2048, 4096, 5120, 6144, 8192, 16384):
         prev = 0
-        for T in [1, 2, 3, 4, 7, 16, 64, 100, 256, 449, 512, 1024, 2048, 4096, 16384, 65536, 131072]:
-            form, chunks = rn.rmsnorm_bwd_route(T, 1, H, 0, 0, 1)
-            assert form == rn.RMSN_FORM_PAIR
-            assert 1 <= chunks <= min(512, T) and chunks >= prev, (H, T, chunks)
-            prev = chunks
-        assert rn.rmsnorm_bwd_route(1, 1, H, 0, 0, 1)[1] == 1
-        assert prev >= 256
+        for T in [1, 2, 3, 4, 7, 16, 64, 100, 256, 384, 449, 512, 768, 1024, 2048, 4096, 16384, 65536, 131072]:
+            r = rn.rmsnorm_bwd_route(T, 1, H, 0, 0, 1)
+            assert r == rn.rmsnorm_bwd_route(T, 1, H, 1, 1, 0)
+            form, chunks, cc, cv = r
+            stage = order[(form, cc == 1)]
+            assert stage >= prev, (H, T, r)
+            prev = stage
+            if form == rn.RMSN_FORM_PAIR:
+                assert 1 <= chunks <= 512 and cc == cv == 0
+            else:
+                assert 1 <= chunks <= min(T, 512 if cc > 1 else T) and cv in (1, 2, 4, 8) and 1 <= cc <= 64
+        assert rn.rmsnorm_bwd_route(1, 1, H, 0, 0, 1)[:3] == (rn.RMSN_FORM_COLS, 1, 1)
+        assert prev == 2 and rn.rmsnorm_bwd_route(65536, 1, H, 0, 0, 1)[1] >= 256
 
 
 def test_row_count_limit_is_below_2_pow_30():

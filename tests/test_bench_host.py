@@ -57,3 +57,51 @@ def test_sweep_shapes_cover_the_pages_tables():
     assert len(names) == len(b.SWEEP_SHAPES) == 115
     assert {"H4096 T65536", "H6144 T1 res w32", "H5120 T321", "H512 T256"} <= names
     assert set(b.shape_name(*s) for s in b.SMALL_T_SHAPES) <= names
+
+
+def test_profile_report_scales_counters_and_averages_the_last_run(tmp_path):
+    b = _bench()
+    W, K = 1, 2
+    fwd = "void rmsn::fwd_kernel<768, 1, 4, false, true, false>(rmsn::FwdParams)"
+    bwd = "void rmsn::bwd_kernel<256, 3, 1, false, false, false>(rmsn::BwdParams)"
+    red = "rmsn::dw_reduce_kernel(double const*, int, int, float*)"
+    copy = "__amd_rocclr_copyBuffer"
+    # W + 2K steps of (fwd, fwd, bwd, reduce); the last K steps are slower
+    events, t = [], 0
+    for step in range(W + 2 * K):
+        d = 1200 if step >= W + K else 1000
+        for name, dur in ((fwd, d), (fwd, d), (bwd, 700), (red, 5)):
+            events.append((name, t, t + dur * 1000))
+            t += dur * 1000 + 100
+    (tmp_path / "ktrace").mkdir()
+    _trace(tmp_path / "ktrace" / "run_kernel_trace.csv", events)
+    with open(tmp_path / "ktrace" / "run_kernel_stats.csv", "w", newline="") as f:
+        w = csv.DictWriter(f, fieldnames=["Name", "Calls", "AverageNs", "MinNs", "MaxNs"])
+        w.writeheader()
+        for name in (fwd, bwd, red):
+            ds = [e - s for n, s, e in events if n == name]
+            w.writerow({"Name": name, "Calls": len(ds), "AverageNs": sum(ds) / len(ds), "MinNs": min(ds),
+                        "MaxNs": max(ds)})
+    for kind, copy_val, per in (("fetch", 524288.0, {fwd: 1000.0, bwd: 500.0, red: 1.0}),
+                                ("write", 1048576.0, {fwd: 2000.0, bwd: 250.0, red: 0.5})):
+        (tmp_path / kind).mkdir()
+        with open(tmp_path / kind / "run_counter_collection.csv", "w", newline="") as f:
+            w = csv.DictWriter(f, fieldnames=["Dispatch_Id", "Kernel_Name", "Counter_Value"])
+            w.writeheader()
+            i = 0
+            for _ in range(3):
+                i += 1
+                w.writerow({"Dispatch_Id": i, "Kernel_Name": copy, "Counter_Value": copy_val})
+            for name, v in per.items():
+                i += 1
+                w.writerow({"Dispatch_Id": i, "Kernel_Name": name, "Counter_Value": v})
+    line = {"roofline": {"us_per_launch_mean": 1200.0}, "roofline_bwd": {"us_per_call_mean": 705.0}}
+    (tmp_path / "ktrace.log").write_text("[bench] x\n" + json.dumps(line) + "\n")
+    md = b.profile_report(str(tmp_path), "T131072_H6144_res", K, W)
+    rec = json.loads(md.split("```json\n")[1].split("\n```")[0])
+    assert abs(rec["fetch_scale"] - 2.0) < 1e-12 and abs(rec["write_scale"] - 1.0) < 1e-12
+    assert rec["kernels"]["fwd_kernel"]["traffic_bytes"] == (1000 * 2 + 2000) * 1024
+    assert rec["trace_last_run_avg_us"]["fwd_kernel"] == 1200.0
+    nb = b.fwd_bytes(131072, 6144, 2, True)
+    assert f"| fwd | {nb:,} |" in md and f"1200.00 ({nb / 1200e-6 / 8e12:.4f})" in md
+    assert "python3 R/bench.py --profile-report OUT T131072_H6144_res 2 1" in md

@@ -17,18 +17,19 @@ import pytest
 
 import oracle
 import synth
-from tests.helpers import (EPS, Layout, Report, check_dw, check_dx, check_fwd, gen_case, to_host_bits,
+from tests.helpers import (EPS, Layout, Report, check_dw, check_dx, check_fwd, gen_case, prepared_bytes, to_host_bits,
                            weight_dev)
 
 pytestmark = pytest.mark.gpu
 
 LAYOUTS = [
-    Layout.plain(301, 2048),                      # row kernel + fixed-order reduce
-    Layout.plain(4099, 1536),                     # prime row count, 512 chunks
-    Layout.plain(3, 4096),                        # one workgroup writes dw itself
-    Layout.heads_view(64, 24, 256, 8192, 256),    # per-head view of a [T, 8192] buffer
+    Layout.plain(301, 2048),                      # one-pass column form
+    Layout.plain(1000, 2048),                     # two-launch column form (row-block partials)
+    Layout.plain(4099, 1536),                     # prime row count, row kernel + fixed-order reduce
+    Layout.plain(3, 4096),                        # one-pass column form, three rows
+    Layout.heads_view(64, 24, 256, 8192, 256),    # per-head view of a [T, 8192] buffer (two-launch column form)
 ]
-IDS = ["T301_H2048", "T4099_H1536", "T3_H4096", "T64x24x256"]
+IDS = ["T301_H2048", "T1000_H2048", "T4099_H1536", "T3_H4096", "T64x24x256"]
 
 
 def _bufs(L, wdt, res, dres, seed):
@@ -167,8 +168,7 @@ def test_atomic_form_needs_only_its_header_zeroed(H):
         check_dw(dw.cpu().numpy(), ref_dw, rep)
         dxs.append(to_host_bits(dx))
     assert all(np.array_equal(dxs[0], d) for d in dxs[1:])
-    acc_bytes = 256 + ((H * 8 + 255) // 256) * 256
-    assert int(ws[:acc_bytes].count_nonzero()) == 0, "atomic form did not leave its header zero"
+    assert int(ws[:prepared_bytes(H)].count_nonzero()) == 0, "atomic form did not leave its header zero"
 
 
 def test_binding_rejects_what_the_abi_cannot_check():

@@ -2,8 +2,11 @@
 the oracle.
 
 Tolerances.  The kernels evaluate silu in FP32: sigmoid(g) = 1 / (1 + exp(-g))
-is within ~4 units in the last place of FP32, so silu and silu' carry a
-relative error below EPS_S = 2^-20 (a margin of ~3 over that bound).
+is within ~4 units in the last place of FP32 while it is a normal number, so
+silu and silu' carry a relative error below EPS_S = 2^-20 (a margin of ~3 over
+that bound); for g < -87.3 sigmoid is FP32-subnormal and its absolute error
+stays below 2^-149 (plus the same relative part), far below the BF16
+subnormal spacing 2^-133 that every check below allows at least.
   * y: within 1 BF16 unit (its FP32 error stays far below half a BF16 unit).
   * rstd: as in the plain forward (the gate does not enter the norm).
   * dx: within 1 BF16 unit, or within one unit plus the bound that silu's
@@ -49,6 +52,10 @@ def gen_gate(seed, R, H, kind):
         gf[1::11] = 0.0                        # closed gate
         gf[2::13] = -1.28125                   # near silu's minimum (silu' ~ 0)
         gf[3::17] = 30.0                       # saturated: silu = g, silu' = 1
+        gf[4::19] = -88.0                      # sigmoid below FP32's normal range
+        gf[5::23] = -90.0
+        gf[6::29] = -100.0                     # silu below BF16's subnormal spacing
+        gf[8::37] = -1.0e4                     # sigmoid underflows to 0
         g = oracle.bf16_round(gf).reshape(R, H)
     return g
 
@@ -84,7 +91,8 @@ def run_gated(L: Layout, wdt="bf16", seed=0, kind="mixed", det_repeats=2):
     xf, gf, df = oracle.bf16_to_f64(x), oracle.bf16_to_f64(g), oracle.bf16_to_f64(dy)
     wf = oracle.bf16_to_f64(w) if wdt == "bf16" else w.astype(np.float64)
     r = rho.astype(np.float64)[:, None]
-    sg = 1.0 / (1.0 + np.exp(-gf))
+    with np.errstate(over="ignore"):
+        sg = 1.0 / (1.0 + np.exp(-gf))
     e = df * gf * sg
     xhat = xf * r
     bx = EPS_S * r * (np.abs(wf * e) + np.abs(xf) * r * r * np.abs(xf * wf * e).sum(1, keepdims=True) / L.H)
@@ -132,6 +140,35 @@ def test_gated_row_counts(T):
 @pytest.mark.parametrize("kind", ["normal", "open", "mixed"])
 def test_gated_gate_families(kind):
     print(kind, run_gated(Layout.plain(2048, 2048), "bf16", seed=7, kind=kind))
+
+
+@pytest.mark.parametrize("H", [64, 2048, 6144])
+def test_gated_infinite_gates_forward(H):
+    # g = -inf gives silu = -inf * 0 = NaN and g = +inf gives +inf, as the
+    # formula g * sigmoid(g) reads in IEEE arithmetic (the oracle's FP64
+    # evaluation and torch's silu agree); the gate never enters the norm, so
+    # rstd and every other element of those rows keep their values
+    import torch
+    import rmsnorm_fwd_amd as rn
+    T = 40
+    x = synth.rows(9, "x", 0, T, H)
+    g = gen_gate(9, T, H, "mixed")
+    gf = oracle.bf16_to_f64(g)
+    gf[::3, 5] = -np.inf
+    gf[1::3, H - 1] = np.inf
+    gf[2::5, 0] = -np.inf
+    g = oracle.bf16_round(gf)
+    w = synth.weight(9, H, "bf16")
+    y, rstd = rn.rmsnorm_gated_fwd(to_dev_bf16(x).view(T, H), to_dev_bf16(g).view(T, H), weight_dev(w), EPS)
+    torch.cuda.synchronize()
+    ref_y, ref_rstd = oracle.gated_fwd_bf16(x, g, w, EPS)
+    yk = to_host_bits(y)
+    yf, rf = oracle.bf16_to_f64(yk), oracle.bf16_to_f64(ref_y)
+    assert np.array_equal(np.isnan(yf), np.isnan(rf)) and np.isnan(rf).sum() == (np.isneginf(gf)).sum()
+    fin = ~np.isnan(rf)
+    assert np.array_equal(yf[~np.isfinite(rf) & fin], rf[~np.isfinite(rf) & fin])
+    assert ulp_dist(yk[np.isfinite(rf)], ref_y[np.isfinite(rf)]).max() <= 1
+    assert (np.abs(rstd.cpu().numpy().astype(np.float64) - ref_rstd) / ref_rstd).max() <= 1e-6
 
 
 def test_gated_head_view():
@@ -198,7 +235,8 @@ def test_gated_full_size_headline_shape():
     _, _, dx64, dg64, _ = oracle.gated_bwd_bf16(x[rows], g[rows], dy[rows], w, rho[rows], want_f64=True)
     xf, gf, df = oracle.bf16_to_f64(x[rows]), oracle.bf16_to_f64(g[rows]), oracle.bf16_to_f64(dy[rows])
     r = rho[rows].astype(np.float64)[:, None]
-    sg = 1.0 / (1.0 + np.exp(-gf))
+    with np.errstate(over="ignore"):
+        sg = 1.0 / (1.0 + np.exp(-gf))
     e = df * gf * sg
     bx = EPS_S * r * (np.abs(w * e) + np.abs(xf) * r * r * np.abs(xf * w * e).sum(1, keepdims=True) / H)
     bg = EPS_S * np.abs(df * xf * r * w) * sg * (1 + 2 * np.abs(gf))
@@ -210,7 +248,8 @@ def test_gated_full_size_headline_shape():
     for r0 in range(0, T, 8192):
         sl = slice(r0, r0 + 8192)
         gb = oracle.bf16_to_f64(g[sl])
-        eb = oracle.bf16_to_f64(dy[sl]) * gb / (1.0 + np.exp(-gb))
+        with np.errstate(over="ignore"):
+            eb = oracle.bf16_to_f64(dy[sl]) * gb / (1.0 + np.exp(-gb))
         absum += np.abs(eb * oracle.bf16_to_f64(x[sl]) * rho[sl].astype(np.float64)[:, None]).sum(0)
     bw = 1e-4 + 1e-4 * np.abs(ref_dw) + EPS_S * absum
     assert (np.abs(dw.cpu().numpy().astype(np.float64) - ref_dw) <= bw).all()

@@ -10,7 +10,8 @@ import torch
 
 import oracle
 import synth
-from tests.helpers import EPS, Report, check_dw, check_dx, check_fwd, to_dev_bf16, to_host_bits, weight_dev
+from tests.helpers import (EPS, Report, check_dw, check_dx, check_fwd, prepared_bytes, to_dev_bf16, to_host_bits,
+                           weight_dev)
 
 pytestmark = pytest.mark.gpu
 
@@ -35,7 +36,7 @@ def test_step_replays_bitwise(T, H, wdt, res, route):
     rstd = torch.empty(T, dtype=torch.float32, device="cuda")
     dw = torch.empty(H, dtype=torch.float32, device="cuda")
     nbytes = (rn.rmsnorm_bwd_workspace_size_for_route(T, 1, H, route) if route
-              else rn.rmsnorm_bwd_workspace_size(T, 1, H))
+              else rn.rmsnorm_bwd_workspace_size(T, 1, H, rn.RMSN_W_F32 if wdt == "f32" else rn.RMSN_W_BF16, res))
     ws = torch.zeros(nbytes, dtype=torch.uint8, device="cuda")
     det = route is None
 
@@ -83,8 +84,7 @@ def test_step_replays_bitwise(T, H, wdt, res, route):
             else:
                 assert np.array_equal(a, b), f"replay {i}: output {k} differs from the eager step"
     if route:
-        acc_bytes = 256 + ((H * 8 + 255) // 256) * 256
-        assert int(ws[:acc_bytes].count_nonzero()) == 0
+        assert int(ws[:prepared_bytes(H)].count_nonzero()) == 0
     print(T, H, wdt, res, route, rep)
 
 
@@ -99,7 +99,7 @@ def test_gated_step_replays_bitwise():
     y, dx, dg = torch.empty_like(x), torch.empty_like(x), torch.empty_like(x)
     rstd = torch.empty(T, dtype=torch.float32, device="cuda")
     dw = torch.empty(H, dtype=torch.float32, device="cuda")
-    ws = torch.zeros(rn.rmsnorm_bwd_workspace_size(T, 1, H), dtype=torch.uint8, device="cuda")
+    ws = torch.zeros(rn.rmsnorm_bwd_workspace_size(T, 1, H, rn.RMSN_W_F32), dtype=torch.uint8, device="cuda")
 
     def step():
         rn.rmsnorm_gated_fwd(x, g, w, EPS, y=y, rstd=rstd)

@@ -85,6 +85,43 @@ def test_closed_gate_and_saturated_gate_reduce_to_plain():
     np.testing.assert_allclose(dg, dy * y0, rtol=1e-14, atol=1e-16)
 
 
+def test_deep_negative_and_infinite_gates():
+    # For g < 0, sigmoid(g) = e^g / (1 + e^g) needs no e^-g, so it stays
+    # accurate (and free of overflow) down to where e^g underflows; silu and
+    # silu' from that form pin the oracle's 1 / (1 + e^-g) far into the
+    # negative tail, where a capped or overflowing exponential goes wrong.
+    # g = -1e4 underflows to -0; g = -inf gives NaN and +inf gives +inf (the
+    # formula g * sigmoid(g) in IEEE arithmetic, like torch's FP64 silu).
+    deep = np.array([-30.0, -88.0, -90.0, -100.0, -300.0, -700.0])
+    R, H = len(deep), 16
+    u, dy = _rand((R, H), 41), _rand((R, H), 42)
+    w = _rand(H, 43, 0.1, 1.0)
+    g = _rand((R, H), 44)
+    g[:, 3] = deep
+    y, rstd = oracle.gated_fwd_f64(u, g, w, EPS)
+    dx, dg, dw = oracle.gated_bwd_f64(u, g, dy, w, rstd)
+    a = u * rstd[:, None] * w
+    t = np.exp(deep)
+    s = t / (1.0 + t)
+    silu = deep * s
+    dsilu = s * (1.0 + deep * (1.0 - s))
+    np.testing.assert_allclose(y[:, 3], a[:, 3] * silu, rtol=1e-14, atol=0)
+    np.testing.assert_allclose(dg[:, 3], dy[:, 3] * a[:, 3] * dsilu, rtol=1e-13, atol=0)
+    assert np.all(y[:, 3] != 0) and np.all(np.abs(y[:, 3]) < 1e-10)
+    np.testing.assert_allclose(y[:, 3], torch.nn.functional.silu(torch.tensor(g)).numpy()[:, 3] * a[:, 3],
+                               rtol=1e-14, atol=0)
+    # underflow and infinities
+    g2 = _rand((3, H), 45)
+    g2[0, 0], g2[1, 1], g2[2, 2] = -1.0e4, -np.inf, np.inf
+    with np.errstate(over="ignore", invalid="ignore"):
+        y2, r2 = oracle.gated_fwd_f64(u[:3], g2, w, EPS)
+    assert y2[0, 0] == 0.0 and np.signbit(y2[0, 0]) != np.signbit(u[0, 0] * w[0])
+    assert np.isnan(y2[1, 1]) and np.isinf(y2[2, 2]) and np.sign(y2[2, 2]) == np.sign(u[2, 2] * w[2])
+    assert np.isfinite(np.delete(y2, [0, 1 * H + 1, 2 * H + 2])).all()
+    ref = torch.nn.functional.silu(torch.tensor(g2)).numpy()
+    assert np.isnan(ref[1, 1]) and np.isinf(ref[2, 2]) and ref[0, 0] == 0.0
+
+
 def test_gated_dx_dw_are_plain_at_the_gated_gradient():
     u, g, dy = _rand((7, 96), 31), _rand((7, 96), 32, 3.0), _rand((7, 96), 33)
     w = _rand(96, 34, 0.1, 1.0)

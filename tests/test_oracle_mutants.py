@@ -38,6 +38,8 @@ MUTANTS = {
     # SiLU-gated variant
     "gate_dropped_f64_fwd": ("ur[j] * s * w[j] * silu(g[r * H + j])", "ur[j] * s * w[j]"),
     "gate_dropped_bf16_fwd": ("u[j] * s * wd[j] * silu(oracle_bf16_to_double(g[o + j]))", "u[j] * s * wd[j]"),
+    "sigmoid_exponent_capped": ("static double sigmoid(double g) { return 1.0 / (1.0 + exp(-g)); }",
+                                "static double sigmoid(double g) { return 1.0 / (1.0 + exp(fmin(-g, 87.0))); }"),
     "silu_is_identity": ("static double silu(double g) { return g * sigmoid(g); }",
                          "static double silu(double g) { return g; }"),
     "silu_grad_sign": ("return sg * (1.0 + g * (1.0 - sg));", "return sg * (1.0 - g * (1.0 - sg));"),

@@ -6,7 +6,7 @@ import pytest
 
 import oracle
 
-from tests.helpers import Layout, run_case
+from tests.helpers import Layout, prepared_bytes, run_case
 
 pytestmark = pytest.mark.gpu
 
@@ -159,6 +159,81 @@ def test_routes_agree(H):
     routes = [(0, 1), (0, 2), (0, 7), (0, 512), (0, 1000), (1, 1), (1, 5), (1, 256)]
     rep = run_case(Layout.plain(333, H), "bf16", seed=21, routes=routes)
     print(H, rep)
+
+
+# column forms: (form, row tasks, row blocks per slice, vectors per slice);
+# row-task and row-block counts above, at and below the row count, every
+# slice width, a ragged last slice where H is not a multiple of the slice
+COLUMN_ROUTES = [(0, 512), (2, 1, 1, 8), (2, 7, 1, 4), (2, 64, 3, 2), (2, 1000, 16, 1), (2, 40, 400, 8),
+                 (3, 13, 2, 8), (3, 5, 5, 4), (3, 300, 64, 1), (3, 2, 333, 2)]
+
+
+@pytest.mark.parametrize("H", [8, 72, 256, 264, 1032, 1536, 2056, 4096, 4104, 6144, 6152, 8200, 16384])
+def test_column_forms_agree(H):
+    # dx bitwise equal to the pair's, dw within budget, for every column route
+    rep = run_case(Layout.plain(333, H), "f32" if H % 16 else "bf16", seed=31 + H, routes=COLUMN_ROUTES)
+    print(H, rep)
+
+
+@pytest.mark.parametrize("layout", [Layout.heads_view(40, 24, 256, 8192, 256), Layout.heads_view(97, 4, 256, 1024, 256),
+                                    Layout.plain(65, 4096, pad=64)], ids=["24x256_s8192", "4x256", "padded"])
+def test_column_forms_on_views_and_residual(layout):
+    rep = run_case(layout, "bf16", res=True, dres=True, seed=5, routes=COLUMN_ROUTES)
+    print(layout, rep)
+
+
+@pytest.mark.parametrize("T,H", [(1, 4096), (5, 2048), (64, 6144), (1000, 1536)])
+def test_column_form_dw_is_the_same_with_and_without_tickets(T, H):
+    """With the same row blocks the deterministic column form (partials summed
+    by the reduce kernel) and the ticket form (summed by the slice's last
+    column task) add the same partials in the same order, and one block per
+    slice needs neither: all give dw bit for bit, over repeated calls."""
+    import torch
+    import rmsnorm_fwd_amd as rn
+    from tests.helpers import gen_case, to_dev_bf16, weight_dev
+    x, _, dy, _, w = gen_case(41, Layout.plain(T, H), "bf16", False, False)
+    X, DY, W = to_dev_bf16(x).view(T, H), to_dev_bf16(dy).view(T, H), weight_dev(w)
+    _, rstd, _ = rn.rmsnorm_fwd(X, W)
+    ws = rn.rmsnorm_bwd_workspace(T, 1, H, "cuda", nbytes=rn.rmsnorm_bwd_workspace_size_for_route(
+        T, 1, H, (2, 8, 16, 2)))
+    for cc in (2, 16):
+        got = []
+        for route, det in [((2, 8, cc, 2), True), ((3, 8, cc, 2), False), ((2, 8, cc, 2), True), ((3, 3, cc, 2), False)]:
+            dx, dw = rn.rmsnorm_bwd_routed(DY, X, rstd, W, route, deterministic=det, workspace=ws)
+            got.append((dx, dw))
+        torch.cuda.synchronize()
+        for dx, dw in got[1:]:
+            assert torch.equal(dx, got[0][0]) and torch.equal(dw, got[0][1])
+    one = [rn.rmsnorm_bwd_routed(DY, X, rstd, W, (2, 4, 1, v), deterministic=True, workspace=ws) for v in (8, 8)]
+    torch.cuda.synchronize()
+    assert torch.equal(one[0][1], one[1][1]) and torch.equal(one[0][0], got[0][0])
+    assert int(ws[:prepared_bytes(H)].count_nonzero()) == 0
+
+
+def _route_edges(heads, H, t_max):
+    """Token counts T where the default route differs from T - 1's."""
+    import rmsnorm_fwd_amd as rn
+    edges, prev = [], rn.rmsnorm_bwd_route(1, heads, H, 0, 0, 1)
+    for T in range(2, t_max + 1):
+        r = rn.rmsnorm_bwd_route(T, heads, H, 0, 0, 1)
+        if r[0] != prev[0] or (r[2] == 1) != (prev[2] == 1):
+            edges.append(T)
+        prev = r
+    return edges
+
+
+@pytest.mark.parametrize("heads,H", [(4, 256), (1, 1536), (1, 4096), (1, 6144), (1, 8192)])
+def test_route_edges_from_both_sides(heads, H):
+    # each change of backward form (one-pass column form -> two-launch column
+    # form -> pair) is run on both sides, in both modes, against the oracle
+    # (p3 commit message: each new edge is exercised from both sides)
+    edges = _route_edges(heads, H, 16384 // heads + 64)
+    assert len(edges) >= 1
+    for T in edges:
+        for t in (T - 1, T):
+            L = Layout.heads_view(t, heads, H, heads * H, H) if heads > 1 else Layout.plain(t, H)
+            rep = run_case(L, "bf16", seed=t, det_repeats=2)
+            print(heads, H, t, rep)
 
 
 def test_deterministic_dw_repeats_at_scale():
