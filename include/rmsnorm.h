@@ -242,6 +242,27 @@ int rmsnorm_bwd_routed(const void* dy, const void* x, const float* rstd, const v
                        int64_t T, int64_t heads, int64_t H, int64_t stride_t, int64_t stride_h,
                        int deterministic, rmsn_route route, void* stream);
 
+/*
+ * rmsnorm_bwd without a workspace argument, for callers that cannot allocate
+ * device memory (code under HIP graph capture, tight serving loops, harnesses
+ * that forbid allocation).  Arguments and results are those of rmsnorm_bwd,
+ * bit for bit (the same route and kernels).  The workspace is the library's
+ * own device scratch of RMSN_NOALLOC_SCRATCH_BYTES per GPU, set up on the
+ * first call on a device (a symbol lookup, and a clear of its prepared part
+ * enqueued on `stream`) and held until the process ends.  Allocates nothing,
+ * ever.  Returns RMSN_ERR_WORKSPACE when the route's workspace
+ * (rmsnorm_bwd_workspace_size) exceeds the scratch -- every width up to
+ * 8192 at every row count fits -- and RMSN_ERR_HIP when the scratch cannot
+ * be set up.  Every call on one GPU shares that GPU's scratch: calls that
+ * may overlap in time on one GPU (different streams, host threads) race and
+ * must be serialised by the caller.
+ */
+#define RMSN_NOALLOC_SCRATCH_BYTES ((size_t)32 << 20)
+int rmsnorm_bwd_noalloc(const void* dy, const void* x, const float* rstd, const void* w, int w_dtype,
+                        const void* residual, void* dx, float* dw,
+                        int64_t T, int64_t heads, int64_t H, int64_t stride_t, int64_t stride_h,
+                        int deterministic, void* stream);
+
 /* Human-readable name of a status code (static storage). */
 const char* rmsnorm_status_string(int status);
 

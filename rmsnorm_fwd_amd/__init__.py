@@ -30,6 +30,7 @@ RMSN_FORM_ATOMIC = 1
 RMSN_FORM_COLS = 2
 RMSN_FORM_COLS_TICKET = 3
 RMSN_MAX_H = 16384
+RMSN_NOALLOC_SCRATCH_BYTES = 32 << 20
 
 # every symbol include/rmsnorm.h declares
 EXPORTS = (
@@ -42,6 +43,7 @@ EXPORTS = (
     "rmsnorm_bwd_routed",
     "rmsnorm_gated_fwd",
     "rmsnorm_gated_bwd",
+    "rmsnorm_bwd_noalloc",
     "rmsnorm_status_string",
 )
 
@@ -94,6 +96,8 @@ def lib() -> ctypes.CDLL:
     L.rmsnorm_gated_bwd.argtypes = [vp, vp, vp, vp, vp, i32, vp, vp, vp, vp, ctypes.c_size_t,
                                     i64, i64, i64, i64, i64, i32, vp]
     L.rmsnorm_gated_bwd.restype = i32
+    L.rmsnorm_bwd_noalloc.argtypes = [vp, vp, vp, vp, i32, vp, vp, vp, i64, i64, i64, i64, i64, i32, vp]
+    L.rmsnorm_bwd_noalloc.restype = i32
     L.rmsnorm_status_string.argtypes = [i32]
     L.rmsnorm_status_string.restype = ctypes.c_char_p
     _lib = L
@@ -311,6 +315,17 @@ def rmsnorm_bwd(dy, x, rstd, w, residual=None, deterministic: bool = True, *,
                             workspace.numel() * workspace.element_size(),
                             T, heads, H, st, sh, int(bool(deterministic)), _stream(x.device, stream))
     _check("rmsnorm_bwd", st_)
+    return dx, dw
+
+
+def rmsnorm_bwd_noalloc(dy, x, rstd, w, residual=None, deterministic: bool = True, *, dx, dw, stream=None):
+    """rmsnorm_bwd on the library's own device scratch: no workspace, and no
+    allocation by the library or here (dx and dw must be given)."""
+    (T, heads, H, st, sh), dx, dw = _bwd_args(dy, x, rstd, w, residual, dx, dw)
+    st_ = lib().rmsnorm_bwd_noalloc(_ptr(dy), _ptr(x), _ptr(rstd), _ptr(w), _w_dtype(w), _ptr(residual),
+                                    _ptr(dx), _ptr(dw), T, heads, H, st, sh, int(bool(deterministic)),
+                                    _stream(x.device, stream))
+    _check("rmsnorm_bwd_noalloc", st_)
     return dx, dw
 
 

@@ -281,6 +281,25 @@ int rmsnorm_bwd(const void* dy, const void* x, const float* rstd, const void* w,
     return bwd_impl(dy, x, rstd, w, w_dtype, residual, dx, dw, workspace, s, r, static_cast<hipStream_t>(stream));
 }
 
+int rmsnorm_bwd_noalloc(const void* dy, const void* x, const float* rstd, const void* w, int w_dtype,
+                        const void* residual, void* dx, float* dw,
+                        int64_t T, int64_t heads, int64_t H, int64_t stride_t, int64_t stride_h,
+                        int deterministic, void* stream)
+{
+    Shape s;
+    int st = check_shape(T, heads, H, stride_t, stride_h, &s);
+    if (st != RMSN_OK) return st;
+    // the scratch stands in for the workspace: validate everything else first
+    alignas(256) static char stand_in;
+    st = check_bwd_args(dy, x, rstd, w, w_dtype, residual, dx, dw, &stand_in, s);
+    if (st != RMSN_OK) return st;
+    const BwdRoute r = default_bwd_route(s.R, s.H, w_dtype == RMSN_W_F32, residual != nullptr, deterministic != 0);
+    if (s.R > 0 && ws_bytes_for(s.R, s.H, r) > kScratchBytes) return RMSN_ERR_WORKSPACE;
+    hipStream_t hs = static_cast<hipStream_t>(stream);
+    void* scratch = nullptr;
+    if (s.R > 0 && scratch_region(&scratch, hs) != hipSuccess) return RMSN_ERR_HIP;
+    return bwd_impl(dy, x, rstd, w, w_dtype, residual, dx, dw, scratch, s, r, hs);
+}
 
 int rmsnorm_gated_bwd(const void* dy, const void* x, const void* gate, const float* rstd, const void* w,
                       int w_dtype, void* dx, void* dgate, float* dw, void* workspace, size_t workspace_bytes,

@@ -44,6 +44,10 @@
 // is e = dy * silu(g): x*dy*silu(g) is still exact in FP64 (16 + 24 bits),
 // so S, dw and dx follow the same arithmetic with e in place of dy, and the
 // kernel also writes dg = dy * (xhat * w) * silu'(g), formed in FP32.
+#include <atomic>
+#include <mutex>
+
+#include "../../include/rmsnorm.h"
 #include "device_common.h"
 #include "kernels.h"
 #include "route.h"
@@ -642,6 +646,45 @@ hipError_t launch_fill_zero(void* ptr, int64_t bytes, hipStream_t s)
     if (blocks > 1024) blocks = 1024;
     hipLaunchKernelGGL(fill_zero_kernel, dim3((int)blocks), dim3(256), 0, s, static_cast<uint32_t*>(ptr), words);
     return hipGetLastError();
+}
+
+// ------------------------------------------------ library-owned scratch ----
+// For callers that cannot allocate (rmsnorm_bwd_noalloc): a file-scope device
+// array, one per GPU the library runs on, held until the process ends.  Host
+// code never uses the array's name as an address (on the host it names a
+// stand-in, not device memory): the device address is looked up with
+// hipGetSymbolAddress once per device, with that device current, and kept.
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::atomic<void*> g_scratch[kMaxDevices];
+std::mutex g_scratch_mu;
+}  // namespace
+
+hipError_t scratch_region(void** out, hipStream_t s)
+{
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+    void* ptr = g_scratch[dev].load(std::memory_order_acquire);
+    if (!ptr) {
+        std::lock_guard<std::mutex> lock(g_scratch_mu);
+        ptr = g_scratch[dev].load(std::memory_order_acquire);
+        if (!ptr) {
+            e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+            if (e != hipSuccess) return e;
+            if (!ptr) return hipErrorInvalidSymbol;
+            // the prepared part (tickets and accumulator) must start at zero;
+            // every call leaves it zero again
+            e = launch_fill_zero(ptr, (int64_t)ws_part_offset(RMSN_MAX_H), s);
+            if (e != hipSuccess) return e;
+            g_scratch[dev].store(ptr, std::memory_order_release);
+        }
+    }
+    *out = ptr;
+    return hipSuccess;
 }
 
 }  // namespace rmsn

@@ -83,5 +83,11 @@ hipError_t launch_bwd_cols(int layout, bool w_f32, const BwdParams& p, bool rows
 hipError_t launch_dw_reduce(const double* part, int chunks, int H, float* dw, hipStream_t s);
 hipError_t launch_fill_zero(void* ptr, int64_t bytes, hipStream_t s);
 
+// The library's own device scratch for callers that cannot allocate: a
+// file-scope device array of kScratchBytes per GPU.  scratch_region returns
+// its device address on the current device (looked up once per device, when
+// its prepared part is also cleared on `s`); hipSuccess or the lookup's error.
+constexpr size_t kScratchBytes = size_t(32) << 20;
+hipError_t scratch_region(void** out, hipStream_t s);
 
 }  // namespace rmsn

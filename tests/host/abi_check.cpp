@@ -12,6 +12,9 @@
 //   * the same for explicit column-form routes (slice tickets inside the
 //     prepared part, row-block partials inside the workspace, the reduce
 //     launched exactly for the deterministic multi-block form);
+//   * rmsnorm_bwd_noalloc runs the route rmsnorm_bwd takes on the scratch,
+//     refuses routes whose workspace exceeds it, and rejects bad arguments
+//     before touching it;
 //   * the forward grid is within [1, compute units * layout cap] and every
 //     launch gets the row count and width it was given.
 // Prints "ok" and exits 0, or prints the first failures and exits 1.
@@ -28,7 +31,7 @@
 namespace rmsn {
 
 struct Calls {
-    int fwd = 0, bwd = 0, cols = 0, cols_rows = 0, cols_col_tasks = 0, reduce = 0, fill = 0;
+    int fwd = 0, bwd = 0, cols = 0, cols_rows = 0, cols_col_tasks = 0, reduce = 0, fill = 0, scratch = 0;
     FwdParams fp{};
     BwdParams bp{};
     int grid = 0, layout = -1, fwd_table = -1, reduce_chunks = 0, reduce_h = 0;
@@ -60,6 +63,13 @@ hipError_t launch_bwd_cols(int layout, bool, const BwdParams& p, bool rows, hipS
     g.cols_col_tasks += p.col_tasks;
     g.bp = p;
     g.layout = layout;
+    return hipSuccess;
+}
+alignas(256) static char fake_scratch[64];
+hipError_t scratch_region(void** out, hipStream_t)
+{
+    ++g.scratch;
+    *out = fake_scratch;
     return hipSuccess;
 }
 hipError_t launch_dw_reduce(const double*, int chunks, int H, float*, hipStream_t)
@@ -200,7 +210,18 @@ static void check_error_paths()
           "dgate misaligned");
     CHECK(rmsnorm_bwd_workspace_init(P(6), ws, 12, nullptr) == RMSN_ERR_INVALID_ARG, "init H = 12");
     CHECK(rmsnorm_bwd_workspace_init(P(6), 100, H, nullptr) == RMSN_ERR_WORKSPACE, "init too small");
-    CHECK(g.bwd == 0 && g.cols == 0 && g.reduce == 0 && g.fill == 0, "a rejected backward launched");
+    // the allocation-free backward: argument errors before the scratch is looked up
+    CHECK(rmsnorm_bwd_noalloc(P(0), P(1), (const float*)P(2), P(3), RMSN_W_F32, nullptr, P(4), nullptr, 64, 1, H, H,
+                              H, 1, nullptr) == RMSN_ERR_INVALID_ARG, "noalloc dw null");
+    CHECK(rmsnorm_bwd_noalloc(P(0), P(1), (const float*)P(2), P(3), 3, nullptr, P(4), (float*)P(5), 64, 1, H, H, H,
+                              1, nullptr) == RMSN_ERR_INVALID_ARG, "noalloc w dtype");
+    CHECK(rmsnorm_bwd_noalloc((char*)P(0) + 2, P(1), (const float*)P(2), P(3), RMSN_W_F32, nullptr, P(4),
+                              (float*)P(5), 64, 1, H, H, H, 1, nullptr) == RMSN_ERR_MISALIGNED, "noalloc dy misaligned");
+    CHECK(rmsnorm_bwd_noalloc(P(0), P(1), (const float*)P(2), P(3), RMSN_W_F32, nullptr, P(4), (float*)P(5), 65536,
+                              1, 16384, 16384, 16384, 1, nullptr) == RMSN_ERR_WORKSPACE,
+          "noalloc route beyond the scratch");
+    CHECK(g.bwd == 0 && g.cols == 0 && g.reduce == 0 && g.fill == 0 && g.scratch == 0,
+          "a rejected backward launched or touched the scratch");
     CHECK(rmsnorm_bwd_workspace_size(4, 1, 12, RMSN_W_BF16, nullptr, 1) == 0 &&
               rmsnorm_bwd_workspace_size(-1, 1, H, RMSN_W_BF16, nullptr, 1) == 0 &&
               rmsnorm_bwd_workspace_size(int64_t(1) << 30, 1, H, RMSN_W_BF16, nullptr, 1) == 0 &&
@@ -301,6 +322,18 @@ static void check_backward_shape(int64_t T, int64_t heads, int64_t H)
                 else
                     CHECK(g.bwd == 1 && g.cols == 0, "in place, the row kernel");
                 check_ws_accesses((const char*)P(6), ws, H, rt.form, "in place");
+                // the allocation-free entry point takes the same route on the scratch
+                reset();
+                const int sn = rmsnorm_bwd_noalloc(P(0), P(1), (const float*)P(2), P(3), wd, dres, P(4), (float*)P(5),
+                                                   T, heads, H, st, sh, det, nullptr);
+                if (ws <= kScratchBytes) {
+                    CHECK(sn == RMSN_OK && g.scratch == 1 && g.bwd + g.cols == 1 && g.bp.form == rt.form &&
+                              g.bp.chunks == rt.chunks && (const char*)g.bp.ticket == fake_scratch,
+                          "noalloc runs the route on the scratch (status %d)", sn);
+                } else {
+                    CHECK(sn == RMSN_ERR_WORKSPACE && g.bwd + g.cols == 0 && g.scratch == 0,
+                          "noalloc refuses a route beyond the scratch");
+                }
             }
 }
 

@@ -163,6 +163,38 @@ def test_routed_rejects_malformed_routes(route, det):
     assert rn.rmsnorm_bwd_workspace_size_for_route(4, 1, 64, route) == 0 or det
 
 
+def _noalloc(**kw):
+    a = dict(dy=GOOD, x=GOOD, rstd=GOOD, w=GOOD, wd=0, dres=None, dx=GOOD, dw=GOOD, T=4, heads=1, H=64, st=64,
+             sh=64, det=1)
+    a.update(kw)
+    return rn.lib().rmsnorm_bwd_noalloc(a["dy"], a["x"], a["rstd"], a["w"], a["wd"], a["dres"], a["dx"], a["dw"],
+                                        a["T"], a["heads"], a["H"], a["st"], a["sh"], a["det"], None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(H=20, st=20, sh=20), rn.RMSN_ERR_UNSUPPORTED),
+    (dict(wd=2), rn.RMSN_ERR_INVALID_ARG),
+    (dict(dw=None), rn.RMSN_ERR_INVALID_ARG),
+    (dict(dy=None), rn.RMSN_ERR_INVALID_ARG),
+    (dict(dx=BAD), rn.RMSN_ERR_MISALIGNED),
+    (dict(dres=BAD), rn.RMSN_ERR_MISALIGNED),
+    (dict(st=32), rn.RMSN_ERR_INVALID_ARG),
+    # H 16384 at 65536 rows routes to 256 chunks x 16384 FP64 partials: beyond the scratch
+    (dict(T=65536, H=16384, st=16384, sh=16384), rn.RMSN_ERR_WORKSPACE),
+])
+def test_noalloc_rejects_bad_arguments(kw, status):
+    # every one of these is refused on the host, before the scratch is touched
+    assert _noalloc(**kw) == status
+
+
+def test_noalloc_scratch_covers_every_width_up_to_8192():
+    for H in range(8, 8193, 8):
+        for T in (1, 64, 4096, 65536, (1 << 30) // 8192 - 1):
+            for det in (0, 1):
+                need = rn.rmsnorm_bwd_workspace_size(T, 1, H, 0, False, det)
+                assert 0 < need <= rn.RMSN_NOALLOC_SCRATCH_BYTES, (H, T, det, need)
+
+
 def test_status_strings():
     for s in range(6):
         assert rn.status_string(s)
