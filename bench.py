@@ -454,6 +454,29 @@ def span_report(trace_csv, seq_path):
     return out
 
 
+def span_markdown(rep, seq_path):
+    """The span report as the committed summary: a table per shape, and the
+    figures as JSON."""
+    ops = ("fwd", "bwd_det", "bwd_nondet", "step_det")
+    out = ["# Kernel spans over the pages' shape list (rocprofv3 kernel trace)", "",
+           "One span = first kernel start to last kernel end of one op, from the GPU timestamps of a rocprofv3 kernel "
+           "trace, after a 1 GiB flush of L2 and the last-level cache (the pages time CUPTI spans of one graph replay "
+           "after an L2 flush).  Median of the spans per op; `k` = kernels per op (the step is fwd + fwd + bwd).  "
+           "The backward's kernels follow the route of each shape: one column-form launch at small T, the column "
+           "form and the fixed-order reduce at mid T, the row kernel and the reduce above.", "",
+           "Commands (from /tmp with TMPDIR=/tmp on one MI355X; R = repository root, OUT = an output directory):", "",
+           "```",
+           "rocprofv3 --kernel-trace --output-format csv -d OUT -o run -- python3 R/bench.py --span-sweep OUT/seq.json",
+           "python3 R/bench.py --span-report OUT/run_kernel_trace.csv OUT/seq.json",
+           "```", "",
+           "| shape | " + " | ".join(f"{o} us (k)" for o in ops) + " |", "|---|" + "---|" * len(ops)]
+    for shape, r in rep.items():
+        cells = [f"{r[o]['median_us']:.2f} ({r[o]['kernels']})" if o in r else "-" for o in ops]
+        out.append(f"| {shape} | " + " | ".join(cells) + " |")
+    out += ["", "```json", json.dumps({"kernel_spans_us": rep}), "```", ""]
+    return "\n".join(out)
+
+
 def _step_oracle(wl, rows):
     """One oracle step over the leading `rows` rows; seconds of its three ops."""
     import oracle
@@ -779,8 +802,7 @@ def main():
     args = ap.parse_args()
 
     if args.span_report:
-        rep = span_report(*args.span_report)
-        print(json.dumps({"kernel_spans_us": rep}))
+        print(span_markdown(span_report(*args.span_report), args.span_report[1]))
         return
     if args.profile_report:
         o, w, k, wu = args.profile_report
