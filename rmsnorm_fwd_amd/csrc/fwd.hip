@@ -166,13 +166,22 @@ template <int LPR, int V, int U>
 static hipError_t fwd_dispatch(bool w_f32, const FwdParams& p, int grid, hipStream_t s)
 {
     if (p.r) return fwd_w<LPR, V, U, true, false>(w_f32, p, grid, s);
-    if (p.g) return fwd_w<LPR, V, U, false, true>(w_f32, p, grid, s);
     return fwd_w<LPR, V, U, false, false>(w_f32, p, grid, s);
 }
 
 hipError_t launch_fwd(int table, int layout, bool w_f32, const FwdParams& p, int grid, hipStream_t s)
 {
-    if ((table == FWD_LONG && (p.r || p.g)) || (table == FWD_RES_LONG && !p.r)) return hipErrorInvalidValue;
+    if ((table == FWD_LONG && (p.r || p.g)) || (table == FWD_RES_LONG && !p.r) || ((table == FWD_GATED) != (p.g != nullptr)))
+        return hipErrorInvalidValue;
+    if (table == FWD_GATED) {
+        switch (layout) {
+#define RMSN_FWD_GATED_CASE(id, mh, l, vv, uu, kk) \
+    case id: return fwd_w<l, vv, uu, false, true>(w_f32, p, grid, s);
+            RMSN_FWD_GATED_LAYOUTS(RMSN_FWD_GATED_CASE)
+#undef RMSN_FWD_GATED_CASE
+        default: return hipErrorInvalidValue;
+        }
+    }
     if (table == FWD_LONG) {
         switch (layout) {
 #define RMSN_FWD_LONG_CASE(id, mh, l, vv, uu, kk) \

@@ -109,6 +109,26 @@ constexpr long long kFwdResLongRows = 32768;
     X(11, 8192, 512, 2, 2, 32)  \
     X(12, 16384, 512, 4, 1, 8)
 
+// The SiLU-gated forward is an operation of its own (its rstd need not equal
+// the plain forward's bits), with its own table: the plain one, except at
+// H 6144, where 256 lanes x 3 vectors and one row per row group beat the
+// plain 768 x 1 (T 65536: 421-425 against 473-478 us; T 16384: 102 against
+// 130 us; 384 x 2: 444 / 118).
+#define RMSN_FWD_GATED_LAYOUTS(X) \
+    X(0, 64, 8, 1, 4, 64)         \
+    X(1, 128, 16, 1, 4, 64)       \
+    X(2, 256, 8, 4, 1, 64)        \
+    X(3, 512, 32, 2, 2, 64)       \
+    X(4, 1024, 32, 4, 1, 64)      \
+    X(5, 1536, 32, 6, 1, 16)      \
+    X(6, 2048, 256, 1, 4, 64)     \
+    X(7, 3072, 64, 6, 1, 32)      \
+    X(8, 4096, 512, 1, 2, 64)     \
+    X(9, 5120, 320, 2, 2, 64)     \
+    X(10, 6144, 256, 3, 1, 32)    \
+    X(11, 8192, 512, 2, 2, 32)    \
+    X(12, 16384, 512, 4, 1, 8)
+
 #define RMSN_BWD_LAYOUTS(X)       \
     X(0, 64, 8, 1, 2, 512)        \
     X(1, 128, 16, 1, 2, 512)      \
@@ -128,6 +148,7 @@ constexpr long long kFwdResLongRows = 32768;
 RMSN_FWD_LAYOUTS(RMSN_CHECK_LAYOUT)
 RMSN_FWD_LONG_LAYOUTS(RMSN_CHECK_LAYOUT)
 RMSN_FWD_RES_LONG_LAYOUTS(RMSN_CHECK_LAYOUT)
+RMSN_FWD_GATED_LAYOUTS(RMSN_CHECK_LAYOUT)
 RMSN_BWD_LAYOUTS(RMSN_CHECK_LAYOUT)
 #undef RMSN_CHECK_LAYOUT
 
@@ -146,12 +167,14 @@ RMSN_BWD_LAYOUTS(RMSN_CHECK_LDS)
 static constexpr Layout kFwdLayouts[] = {RMSN_FWD_LAYOUTS(RMSN_LAYOUT_ENTRY)};
 static constexpr Layout kFwdLongLayouts[] = {RMSN_FWD_LONG_LAYOUTS(RMSN_LAYOUT_ENTRY)};
 static constexpr Layout kFwdResLongLayouts[] = {RMSN_FWD_RES_LONG_LAYOUTS(RMSN_LAYOUT_ENTRY)};
+static constexpr Layout kFwdGatedLayouts[] = {RMSN_FWD_GATED_LAYOUTS(RMSN_LAYOUT_ENTRY)};
 static constexpr Layout kBwdLayouts[] = {RMSN_BWD_LAYOUTS(RMSN_LAYOUT_ENTRY)};
 #undef RMSN_LAYOUT_ENTRY
 
 static constexpr int kNumFwdLayouts = sizeof(kFwdLayouts) / sizeof(kFwdLayouts[0]);
 static_assert(sizeof(kFwdResLongLayouts) == sizeof(kFwdLayouts), "one residual layout per forward layout");
 static_assert(sizeof(kFwdLongLayouts) == sizeof(kFwdLayouts), "one long-run layout per forward layout");
+static_assert(sizeof(kFwdGatedLayouts) == sizeof(kFwdLayouts), "one gated layout per forward layout");
 
 // Same widths, lanes and vectors per row in every forward table.
 constexpr bool fwd_tables_agree(const Layout* t, int i = 0)
@@ -162,19 +185,21 @@ constexpr bool fwd_tables_agree(const Layout* t, int i = 0)
 static_assert(fwd_tables_agree(kFwdResLongLayouts), "the residual forward keeps the plain forward's row layout");
 static_assert(fwd_tables_agree(kFwdLongLayouts), "long runs keep the plain forward's row layout");
 
-// Which forward table serves a call: the long-run tables for plain
-// (ungated) forwards over at least kFwdLongRows rows and residual forwards
-// over at least kFwdResLongRows rows; else the plain table, which serves the
-// plain, gated and residual kernels alike.
-enum { FWD_PLAIN = 0, FWD_LONG = 1, FWD_RES_LONG = 2 };
+// Which forward table serves a call: the gated table for gated forwards;
+// the long-run tables for plain forwards over at least kFwdLongRows rows and
+// residual forwards over at least kFwdResLongRows rows; else the plain
+// table, which serves the plain and residual kernels alike.
+enum { FWD_PLAIN = 0, FWD_LONG = 1, FWD_RES_LONG = 2, FWD_GATED = 3 };
 inline int fwd_table_kind(long long R, bool residual, bool gated)
 {
+    if (gated) return FWD_GATED;
     if (residual) return R >= kFwdResLongRows ? FWD_RES_LONG : FWD_PLAIN;
-    return (!gated && R >= kFwdLongRows) ? FWD_LONG : FWD_PLAIN;
+    return R >= kFwdLongRows ? FWD_LONG : FWD_PLAIN;
 }
 inline const Layout* fwd_table(int kind)
 {
-    return kind == FWD_RES_LONG ? kFwdResLongLayouts : (kind == FWD_LONG ? kFwdLongLayouts : kFwdLayouts);
+    return kind == FWD_GATED ? kFwdGatedLayouts
+                             : (kind == FWD_RES_LONG ? kFwdResLongLayouts : (kind == FWD_LONG ? kFwdLongLayouts : kFwdLayouts));
 }
 static constexpr int kNumBwdLayouts = sizeof(kBwdLayouts) / sizeof(kBwdLayouts[0]);
 

@@ -93,10 +93,16 @@ BwdRoute pair_route(int64_t R, int64_t H)
     // otherwise cost more than the rows themselves.  Measured at H 1536 to
     // 6144, T 256 to 2048: 4 rows per workgroup, but never fewer than 128
     // workgroups, is best or within 1.4 us of the best count.
+    // Up to R * H = 12 M elements 384 workgroups beat 512 (T 4096, H 1536:
+    // 18.8 against 19.6 us; T 2048, H 5120: 28.1 against 28.6 us, the same
+    // in two runs), above that 512 (T 6144, H 5120: 48.1 against 52.2 us).
+    // Halving the partials' bytes with FP32 partials was slower at every
+    // size (19.6 -> 26.9 us; 263 -> 266 us at T 65536, H 4096).
     const int64_t per = (4 + rpi - 1) / rpi;  // row groups per workgroup
     int64_t c = (groups + per - 1) / per;
     if (c < 128) c = groups < 128 ? groups : 128;
-    if (c > L.k) c = L.k;
+    const int64_t cap = R * H <= 12000000 && L.k > 384 ? 384 : L.k;
+    if (c > cap) c = cap;
     return BwdRoute{FORM_PAIR, (int)(c > 0 ? c : 1), 0, 0};
 }
 

@@ -386,7 +386,7 @@ static void check_forward_shape(int64_t T, int64_t heads, int64_t H, bool residu
     CHECK((g.fp.r != nullptr) == residual && (g.fp.h != nullptr) == residual, "forward residual pointers");
 }
 
-// The gated forward always takes the plain table, whatever the row count.
+// The gated forward always takes its own table, whatever the row count.
 static void check_gated_forward_table()
 {
     const int64_t Ts[] = {1, 32768, 65535, 65536, 131072};
@@ -394,7 +394,7 @@ static void check_gated_forward_table()
         reset();
         const int st = rmsnorm_gated_fwd(P(0), P(4), P(1), RMSN_W_BF16, P(2), (float*)P(3), T, 1, 4096, 4096, 4096,
                                          1e-6, 1, nullptr);
-        CHECK(st == RMSN_OK && g.fwd == 1 && g.fwd_table == FWD_PLAIN && g.fp.g != nullptr,
+        CHECK(st == RMSN_OK && g.fwd == 1 && g.fwd_table == FWD_GATED && g.fp.g != nullptr,
               "gated forward table for T=%lld", (long long)T);
     }
 }

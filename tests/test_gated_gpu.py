@@ -10,8 +10,10 @@ subnormal spacing 2^-133 that every check below allows at least.
   * y: within 1 BF16 unit (its FP32 error stays far below half a BF16 unit).
   * rstd: as in the plain forward (the gate does not enter the norm).
   * dx: within 1 BF16 unit, or within one unit plus the bound that silu's
-    error sets on the FP64 evaluation: EPS_S * rho * (|w e| + |x| rho^2
-    sum_i |x_i w_i e_i| / H), e = dy * silu(g).
+    error sets: EPS_S * rho * (|w e| + |x| rho^2 sum_i |x_i w_i e_i| / H),
+    e = dy * silu(g).  The kernel forms the gated dx in FP32 (and rounds
+    x * dy * silu(g) once in FP32 before its FP64 sums): those roundings,
+    ~3 * 2^-24 of the same terms, sit inside that bound.
   * dg: within 1 BF16 unit, or one unit plus EPS_S * |dy * xhat * w| *
     sigmoid(g) * (1 + 2 |g|) (silu' = sigmoid (1 + g (1 - sigmoid)) cancels
     near g = -1.28).
