@@ -132,8 +132,8 @@ class Workload:
         self.dx = self.view(place(self.x_h))
         self.rstd = torch.empty(self.R, dtype=torch.float32, device=dev)
         self.dw = torch.empty(H, dtype=torch.float32, device=dev)
-        self.ws = rn.rmsnorm_bwd_workspace(T, heads, H, dev, w_dtype=rn.RMSN_W_F32 if wdt == "f32" else rn.RMSN_W_BF16,
-                                           has_residual=res)
+        # one workspace for the calls with and without dres
+        self.ws = rn.rmsnorm_bwd_workspace(T, heads, H, dev, w_dtype=rn.RMSN_W_F32 if wdt == "f32" else rn.RMSN_W_BF16)
         self.fwd_bytes = fwd_bytes(self.R, H, self.sw, res, self.gate)
         self.bwd_bytes = bwd_bytes(self.R, H, self.sw, False, self.gate)
         self.step_bytes = 2 * self.fwd_bytes + self.bwd_bytes
@@ -317,8 +317,8 @@ class DeviceCase:
         self.dx = torch.empty_like(self.x)
         self.rstd = torch.empty(T, dtype=torch.float32, device="cuda")
         self.dw = torch.empty(H, dtype=torch.float32, device="cuda")
-        self.ws = rn.rmsnorm_bwd_workspace(T, 1, H, "cuda", w_dtype=rn.RMSN_W_F32 if wdt == "f32" else rn.RMSN_W_BF16,
-                                           has_residual=res)
+        # one workspace for the calls with and without dres
+        self.ws = rn.rmsnorm_bwd_workspace(T, 1, H, "cuda", w_dtype=rn.RMSN_W_F32 if wdt == "f32" else rn.RMSN_W_BF16)
 
     def fwd(self):
         self.rn.rmsnorm_fwd(self.x, self.w, EPS, residual=self.r, y=self.y, residual_out=self.h,
@@ -623,12 +623,18 @@ def cold_latencies(wl, args, flush):
 
 
 def route_of(wl, rn):
+    """The backward routes of the step (dres NULL; the gated backward's own
+    for a gated workload) in both modes, and with a residual the
+    deterministic route of the backward with dres."""
     route = {}
     names = {0: "pair", 1: "atomic", 2: "cols", 3: "cols_ticket"}
-    for det in (1, 0):
-        f, chunks, cc, cv = rn.rmsnorm_bwd_route(wl.T, wl.heads, wl.H, 1 if wl.wdt == "f32" else 0, wl.res, det)
-        route["det" if det else "nondet"] = {"form": names.get(f, f), "chunks": chunks, "col_chunks": cc,
-                                             "col_vecs": cv}
+    wd = 1 if wl.wdt == "f32" else 0
+    for key, det, dres in (("det", 1, False), ("nondet", 0, False), ("det_dres", 1, True)):
+        if dres and not wl.res:
+            continue
+        f, chunks, cc, cv, pf = (rn.rmsnorm_gated_bwd_route(wl.T, wl.heads, wl.H, wd, det) if wl.gate else
+                                 rn.rmsnorm_bwd_route(wl.T, wl.heads, wl.H, wd, dres, det))
+        route[key] = {"form": names.get(f, f), "chunks": chunks, "col_chunks": cc, "col_vecs": cv, "prefetch": pf}
     return route
 
 

@@ -103,8 +103,11 @@ int rmsnorm_fwd(const void* x, const void* residual, const void* w, int w_dtype,
  *                whether it is NULL matters (it is never dereferenced).
  *   deterministic the backward's flag.
  * The size is that of the route rmsnorm_bwd takes for the same arguments
- * (rmsnorm_bwd_route), so a workspace sized for one mode may be too small
- * for the other: size it with both flags (the larger) to share it.  A pure
+ * (rmsnorm_bwd_route), and with residual NULL at least that of the route
+ * rmsnorm_gated_bwd takes for the same shape, so one size serves both.  A
+ * workspace sized for one mode, or for a non-NULL residual, may be too small
+ * for the other mode, or for residual NULL: size it with both (the larger)
+ * to share it.  A pure
  * function of its arguments; it makes no HIP call.  Always at least the
  * prepared part of rmsnorm_bwd_workspace_init; returns 0 when the shape or
  * w_dtype is invalid or unsupported.
@@ -215,6 +218,13 @@ int rmsnorm_gated_bwd(const void* dy, const void* x, const void* gate, const flo
  *   col_chunks, col_vecs  column forms only (0 for the others): row blocks
  *          per column slice, 1 .. 4096; 16-byte vectors per slice: 1, 2, 4
  *          or 8.
+ *   prefetch  pair and atomic forms: 1 makes each row-kernel workgroup load
+ *          its next rows while it reduces the current ones (a second
+ *          register tile; pays where a compute unit holds few workgroups);
+ *          0 or 1, and 0 for the column forms.  A scheduling choice only: it
+ *          changes no bit of dx or dw.  It has no effect with chunks = 1 or
+ *          on the gated backward, whose rows of one vector per lane always
+ *          load ahead.
  * The per-row work, and so dx, does not depend on the route.
  */
 enum rmsn_form { RMSN_FORM_PAIR = 0, RMSN_FORM_ATOMIC = 1, RMSN_FORM_COLS = 2, RMSN_FORM_COLS_TICKET = 3 };
@@ -224,11 +234,18 @@ typedef struct rmsn_route {
     int32_t chunks;
     int32_t col_chunks;
     int32_t col_vecs;
+    int32_t prefetch;
 } rmsn_route;
 
 /* The route rmsnorm_bwd takes for these arguments.  Returns a status. */
 int rmsnorm_bwd_route(int64_t T, int64_t heads, int64_t H, int w_dtype, int has_residual,
                       int deterministic, rmsn_route* out);
+
+/* The route rmsnorm_gated_bwd takes: the plain backward's forms, with the
+ * pair's chunk counts measured for the gated rows (no next-row tile window;
+ * prefetch is always 0).  Returns a status. */
+int rmsnorm_gated_bwd_route(int64_t T, int64_t heads, int64_t H, int w_dtype, int deterministic,
+                            rmsn_route* out);
 
 /* Workspace bytes for an explicit route (0 when invalid). */
 size_t rmsnorm_bwd_workspace_size_for_route(int64_t T, int64_t heads, int64_t H, rmsn_route route);

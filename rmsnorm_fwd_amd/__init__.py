@@ -39,6 +39,7 @@ EXPORTS = (
     "rmsnorm_bwd_workspace_init",
     "rmsnorm_bwd",
     "rmsnorm_bwd_route",
+    "rmsnorm_gated_bwd_route",
     "rmsnorm_bwd_workspace_size_for_route",
     "rmsnorm_bwd_routed",
     "rmsnorm_gated_fwd",
@@ -49,10 +50,11 @@ EXPORTS = (
 
 
 class RmsnRoute(ctypes.Structure):
-    """(form, chunks, col_chunks, col_vecs); the last two are 0 except for
-    the column forms."""
+    """(form, chunks, col_chunks, col_vecs, prefetch); col_chunks and
+    col_vecs are 0 except for the column forms, prefetch 0 or 1 (pair and
+    atomic forms only).  Fields left out of a shorter tuple are 0."""
     _fields_ = [("form", ctypes.c_int32), ("chunks", ctypes.c_int32), ("col_chunks", ctypes.c_int32),
-                ("col_vecs", ctypes.c_int32)]
+                ("col_vecs", ctypes.c_int32), ("prefetch", ctypes.c_int32)]
 
 
 class RmsnError(RuntimeError):
@@ -85,7 +87,9 @@ def lib() -> ctypes.CDLL:
                               i64, i64, i64, i64, i64, i32, vp]
     L.rmsnorm_bwd.restype = i32
     L.rmsnorm_bwd_route.argtypes = [i64, i64, i64, i32, i32, i32, ctypes.POINTER(RmsnRoute)]
+    L.rmsnorm_gated_bwd_route.argtypes = [i64, i64, i64, i32, i32, ctypes.POINTER(RmsnRoute)]
     L.rmsnorm_bwd_route.restype = i32
+    L.rmsnorm_gated_bwd_route.restype = i32
     L.rmsnorm_bwd_workspace_size_for_route.argtypes = [i64, i64, i64, RmsnRoute]
     L.rmsnorm_bwd_workspace_size_for_route.restype = ctypes.c_size_t
     L.rmsnorm_bwd_routed.argtypes = [vp, vp, vp, vp, i32, vp, vp, vp, vp, ctypes.c_size_t,
@@ -253,15 +257,17 @@ def rmsnorm_bwd_workspace_init(workspace, H: int, stream=None):
 
 
 def rmsnorm_bwd_workspace(T: int, heads: int, H: int, device, deterministic=None, nbytes=None,
-                          w_dtype: int = RMSN_W_BF16, has_residual: bool = False):
+                          w_dtype: int = RMSN_W_BF16, has_residual=None):
     """A zero-filled (hence prepared) workspace tensor for rmsnorm_bwd.  With
-    deterministic=None it serves both modes (the larger of the two sizes)."""
+    deterministic=None it serves both modes, with has_residual=None calls
+    with and without dres (the largest of the sizes)."""
     torch = _torch()
     if nbytes is not None:
         n = nbytes
     else:
         modes = (True, False) if deterministic is None else (bool(deterministic),)
-        sizes = [rmsnorm_bwd_workspace_size(T, heads, H, w_dtype, has_residual, d) for d in modes]
+        resid = (False, True) if has_residual is None else (bool(has_residual),)
+        sizes = [rmsnorm_bwd_workspace_size(T, heads, H, w_dtype, r, d) for d in modes for r in resid]
         n = 0 if min(sizes) == 0 else max(sizes)
     if n == 0:
         raise ValueError("unsupported shape")
@@ -270,11 +276,19 @@ def rmsnorm_bwd_workspace(T: int, heads: int, H: int, device, deterministic=None
 
 def rmsnorm_bwd_route(T: int, heads: int, H: int, w_dtype: int, has_residual: bool,
                       deterministic: bool):
-    """The route rmsnorm_bwd takes: (form, chunks, col_chunks, col_vecs)."""
+    """The route rmsnorm_bwd takes: (form, chunks, col_chunks, col_vecs, prefetch)."""
     r = RmsnRoute()
     _check("rmsnorm_bwd_route", lib().rmsnorm_bwd_route(T, heads, H, int(w_dtype), int(bool(has_residual)),
                                                         int(bool(deterministic)), ctypes.byref(r)))
-    return int(r.form), int(r.chunks), int(r.col_chunks), int(r.col_vecs)
+    return int(r.form), int(r.chunks), int(r.col_chunks), int(r.col_vecs), int(r.prefetch)
+
+
+def rmsnorm_gated_bwd_route(T: int, heads: int, H: int, w_dtype: int, deterministic: bool):
+    """The route rmsnorm_gated_bwd takes: (form, chunks, col_chunks, col_vecs, prefetch)."""
+    r = RmsnRoute()
+    _check("rmsnorm_gated_bwd_route", lib().rmsnorm_gated_bwd_route(T, heads, H, int(w_dtype), int(bool(deterministic)),
+                                                                    ctypes.byref(r)))
+    return int(r.form), int(r.chunks), int(r.col_chunks), int(r.col_vecs), int(r.prefetch)
 
 
 def rmsnorm_bwd_workspace_size_for_route(T: int, heads: int, H: int, route) -> int:
@@ -331,8 +345,9 @@ def rmsnorm_bwd_noalloc(dy, x, rstd, w, residual=None, deterministic: bool = Tru
 
 def rmsnorm_bwd_routed(dy, x, rstd, w, route, residual=None, deterministic: bool = True, *,
                        dx=None, dw=None, workspace=None, stream=None):
-    """rmsnorm_bwd with an explicit route: (form, chunks) for the pair and
-    atomic forms, (form, chunks, col_chunks, col_vecs) for the column forms."""
+    """rmsnorm_bwd with an explicit route: (form, chunks) or (form, chunks,
+    0, 0, prefetch) for the pair and atomic forms, (form, chunks, col_chunks,
+    col_vecs) for the column forms."""
     (T, heads, H, st, sh), dx, dw = _bwd_args(dy, x, rstd, w, residual, dx, dw)
     if workspace is None:
         workspace = rmsnorm_bwd_workspace(T, heads, H, x.device, deterministic,

@@ -63,7 +63,7 @@ int cu_count()
 
 int status_of(hipError_t e) { return e == hipSuccess ? RMSN_OK : RMSN_ERR_HIP; }
 
-BwdRoute internal(const rmsn_route& r) { return BwdRoute{r.form, r.chunks, r.col_chunks, r.col_vecs}; }
+BwdRoute internal(const rmsn_route& r) { return BwdRoute{r.form, r.chunks, r.col_chunks, r.col_vecs, r.prefetch}; }
 
 int bwd_impl(const void* dy, const void* x, const float* rstd, const void* w, int w_dtype,
              const void* dres, void* dx, float* dw, void* workspace,
@@ -94,6 +94,7 @@ int bwd_impl(const void* dy, const void* x, const float* rstd, const void* w, in
     p.chunks = r.chunks;
     p.form = r.form;
     p.direct_dw = r.form == FORM_PAIR && r.chunks == 1;
+    p.prefetch = r.prefetch;
     p.inv_h = 1.0 / (double)s.H;
     const bool w32 = w_dtype == RMSN_W_F32;
     if (r.form == FORM_COLS || r.form == FORM_COLS_TICKET) {
@@ -213,7 +214,7 @@ size_t rmsnorm_bwd_workspace_size(int64_t T, int64_t heads, int64_t H, int w_dty
     if (w_dtype != RMSN_W_BF16 && w_dtype != RMSN_W_F32) return 0;
     if (!rows_ok(T, heads) || H < 1 || H % 8 != 0 || H > RMSN_MAX_H) return 0;
     const int64_t R = T * heads;
-    return ws_bytes_for(R, H, default_bwd_route(R, H, w_dtype == RMSN_W_F32, residual != nullptr, deterministic != 0));
+    return bwd_workspace_bytes(R, H, w_dtype == RMSN_W_F32, residual != nullptr, deterministic != 0);
 }
 
 size_t rmsnorm_bwd_workspace_size_for_route(int64_t T, int64_t heads, int64_t H, rmsn_route route)
@@ -233,19 +234,34 @@ int rmsnorm_bwd_workspace_init(void* workspace, size_t workspace_bytes, int64_t 
     return status_of(launch_fill_zero(workspace, (int64_t)need, static_cast<hipStream_t>(stream)));
 }
 
-int rmsnorm_bwd_route(int64_t T, int64_t heads, int64_t H, int w_dtype, int has_residual,
-                      int deterministic, rmsn_route* out)
+static int route_query(int64_t T, int64_t heads, int64_t H, int w_dtype, int has_residual, int deterministic,
+                       bool gated, rmsn_route* out)
 {
     if (!out) return RMSN_ERR_INVALID_ARG;
     if (w_dtype != RMSN_W_BF16 && w_dtype != RMSN_W_F32) return RMSN_ERR_INVALID_ARG;
     if (!rows_ok(T, heads) || H < 1) return RMSN_ERR_INVALID_ARG;
     if (H % 8 != 0 || H > RMSN_MAX_H) return RMSN_ERR_UNSUPPORTED;
-    const BwdRoute r = default_bwd_route(T * heads, H, w_dtype == RMSN_W_F32, has_residual != 0, deterministic != 0);
+    const bool w32 = w_dtype == RMSN_W_F32;
+    const BwdRoute r = gated ? gated_bwd_route(T * heads, H, w32, deterministic != 0)
+                             : default_bwd_route(T * heads, H, w32, has_residual != 0, deterministic != 0);
     out->form = r.form;
     out->chunks = r.chunks;
     out->col_chunks = r.col_chunks;
     out->col_vecs = r.col_vecs;
+    out->prefetch = r.prefetch;
     return RMSN_OK;
+}
+
+int rmsnorm_bwd_route(int64_t T, int64_t heads, int64_t H, int w_dtype, int has_residual,
+                      int deterministic, rmsn_route* out)
+{
+    return route_query(T, heads, H, w_dtype, has_residual, deterministic, false, out);
+}
+
+int rmsnorm_gated_bwd_route(int64_t T, int64_t heads, int64_t H, int w_dtype, int deterministic,
+                            rmsn_route* out)
+{
+    return route_query(T, heads, H, w_dtype, 0, deterministic, true, out);
 }
 
 int rmsnorm_bwd_routed(const void* dy, const void* x, const float* rstd, const void* w, int w_dtype,
@@ -313,7 +329,7 @@ int rmsnorm_gated_bwd(const void* dy, const void* x, const void* gate, const flo
     if (st != RMSN_OK) return st;
     if (s.R > 0 && (!gate || !dgate)) return RMSN_ERR_INVALID_ARG;
     if (s.R > 0 && (!aligned(gate, 16) || !aligned(dgate, 16))) return RMSN_ERR_MISALIGNED;
-    const BwdRoute r = default_bwd_route(s.R, s.H, w_dtype == RMSN_W_F32, false, deterministic != 0);
+    const BwdRoute r = gated_bwd_route(s.R, s.H, w_dtype == RMSN_W_F32, deterministic != 0);
     if (s.R > 0 && workspace_bytes < ws_bytes_for(s.R, s.H, r)) return RMSN_ERR_WORKSPACE;
     return bwd_impl(dy, x, rstd, w, w_dtype, nullptr, dx, dw, workspace, s, r, static_cast<hipStream_t>(stream),
                     gate, dgate);

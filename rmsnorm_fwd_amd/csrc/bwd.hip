@@ -123,7 +123,7 @@ __device__ __forceinline__ void bwd_load(BwdTile<U, V, DRES, GATE>& t, const Bwd
 // measured 1.1-1.25x over contiguous chunks of rows on MI355X).  Writes dx
 // (and dg) for those rows; with DW it also adds each row's dy * xhat into
 // the lane's column sums acc (which it first sets to zero).
-template <int LPR, int V, int U, bool WF32, bool DRES, bool GATE, bool DW>
+template <int LPR, int V, int U, bool WF32, bool DRES, bool GATE, bool DW, bool PFP = false>
 __device__ __forceinline__ void bwd_rows(const BwdParams& p, int chunk, int nchunks, double (&acc)[V][8])
 {
     constexpr int BLOCK = block_of(LPR);
@@ -140,20 +140,18 @@ __device__ __forceinline__ void bwd_rows(const BwdParams& p, int chunk, int nchu
     const int step = nchunks * RPI;
     const int row1 = p.R;
 
-    double w64[V][8];
+    // weights as loaded (FP32: two float4 per vector; BF16: one uint4 in wa)
+    float4 wa[V], wb[WF32 ? V : 1];
 #pragma unroll
     for (int v = 0; v < V; ++v) {
-        float wv[8];
         if constexpr (WF32) {
             const float4* q = reinterpret_cast<const float4*>(static_cast<const float*>(p.w) + lv.col[v]);
-            const float4 a = q[0], b = q[1];
-            wv[0] = a.x; wv[1] = a.y; wv[2] = a.z; wv[3] = a.w;
-            wv[4] = b.x; wv[5] = b.y; wv[6] = b.z; wv[7] = b.w;
+            wa[v] = q[0];
+            wb[v] = q[1];
         } else {
-            unpack8(ld16(static_cast<const uint16_t*>(p.w) + lv.col[v]), wv);
+            const uint4 r = ld16(static_cast<const uint16_t*>(p.w) + lv.col[v]);
+            wa[v] = *reinterpret_cast<const float4*>(&r);
         }
-#pragma unroll
-        for (int e = 0; e < 8; ++e) w64[v][e] = lv.ok[v] ? (double)wv[e] : 0.0;
     }
     if constexpr (DW) {
 #pragma unroll
@@ -162,15 +160,31 @@ __device__ __forceinline__ void bwd_rows(const BwdParams& p, int chunk, int nchu
             for (int e = 0; e < 8; ++e) acc[v][e] = 0.0;
     }
 
-    // Gated rows of one vector per lane load the workgroup's next rows while
-    // the current ones are reduced (a second register tile): their
+    // With PF the workgroup loads its next rows while the current ones are
+    // reduced (a second register tile), the first rows before the weights
+    // are widened.  Gated rows of one vector per lane always do: their
     // workgroups fill a compute unit alone, so no other wavefront covers the
     // load latency, and the tile fits the registers that occupancy leaves.
-    constexpr bool PF = GATE && V == 1;
+    // Plain rows do when the route asks (PFP): where each compute unit holds
+    // few workgroups, as at a few thousand rows.  Results do not depend on it.
+    constexpr bool PF = GATE ? V == 1 : PFP;
     BwdTile<U, V, DRES, GATE> cur;
     BwdTile<PF ? U : 1, PF ? V : 1, DRES, GATE> nxt;
     if constexpr (PF) {
         if (first < row1) bwd_load<U, V, SLOTS, DRES, GATE>(cur, p, lv, first, slot, row1);
+    }
+    double w64[V][8];
+#pragma unroll
+    for (int v = 0; v < V; ++v) {
+        float wv[8];
+        if constexpr (WF32) {
+            wv[0] = wa[v].x; wv[1] = wa[v].y; wv[2] = wa[v].z; wv[3] = wa[v].w;
+            wv[4] = wb[v].x; wv[5] = wb[v].y; wv[6] = wb[v].z; wv[7] = wb[v].w;
+        } else {
+            unpack8(*reinterpret_cast<const uint4*>(&wa[v]), wv);
+        }
+#pragma unroll
+        for (int e = 0; e < 8; ++e) w64[v][e] = lv.ok[v] ? (double)wv[e] : 0.0;
     }
     int it = 0;
     for (int base = first; base < row1; base += step, ++it) {
@@ -264,7 +278,7 @@ __device__ __forceinline__ void bwd_rows(const BwdParams& p, int chunk, int nchu
     }
 }
 
-template <int LPR, int V, int U, bool WF32, bool DRES, bool GATE>
+template <int LPR, int V, int U, bool WF32, bool DRES, bool GATE, bool PFP>
 __global__ void __launch_bounds__(block_of(LPR)) bwd_kernel(BwdParams p)
 {
     constexpr int BLOCK = block_of(LPR);
@@ -274,7 +288,7 @@ __global__ void __launch_bounds__(block_of(LPR)) bwd_kernel(BwdParams p)
 
     const int chunk = blockIdx.x;
     double acc[V][8];
-    bwd_rows<LPR, V, U, WF32, DRES, GATE, true>(p, chunk, p.chunks, acc);
+    bwd_rows<LPR, V, U, WF32, DRES, GATE, true, PFP>(p, chunk, p.chunks, acc);
 
     const int tid = threadIdx.x;
     const int g = tid % LPR;
@@ -522,21 +536,21 @@ __global__ void fill_zero_kernel(uint32_t* p, int64_t words)
 
 // ----------------------------------------------------------- launchers ----
 
-template <int LPR, int V, int U, bool WF32, bool DRES, bool GATE>
+template <int LPR, int V, int U, bool WF32, bool DRES, bool GATE, bool PFP>
 static hipError_t bwd_t(const BwdParams& p, hipStream_t s)
 {
     constexpr int SLOTS = slots_of(LPR);
     constexpr int ROWS = LPR < 64 ? block_of(LPR) / 64 : SLOTS;
     const size_t lds = SLOTS > 1 ? (size_t)ROWS * p.H * sizeof(double) : 0;
     if (lds > (size_t)kMaxSlotLds) return hipErrorInvalidConfiguration;
-    hipLaunchKernelGGL((bwd_kernel<LPR, V, U, WF32, DRES, GATE>), dim3(p.chunks), dim3(block_of(LPR)), lds, s, p);
+    hipLaunchKernelGGL((bwd_kernel<LPR, V, U, WF32, DRES, GATE, PFP>), dim3(p.chunks), dim3(block_of(LPR)), lds, s, p);
     return hipGetLastError();
 }
 
-template <int LPR, int V, int U, bool DRES, bool GATE>
+template <int LPR, int V, int U, bool DRES, bool GATE, bool PFP = false>
 static hipError_t bwd_w(bool w_f32, const BwdParams& p, hipStream_t s)
 {
-    return w_f32 ? bwd_t<LPR, V, U, true, DRES, GATE>(p, s) : bwd_t<LPR, V, U, false, DRES, GATE>(p, s);
+    return w_f32 ? bwd_t<LPR, V, U, true, DRES, GATE, PFP>(p, s) : bwd_t<LPR, V, U, false, DRES, GATE, PFP>(p, s);
 }
 
 // Gated rows hold one more input per element and evaluate silu twice: with
@@ -561,12 +575,14 @@ static hipError_t bwd_gated(bool w_f32, const BwdParams& p, hipStream_t s)
     else return bwd_w<LPR, V, gated_u<LPR, V, U>(), false, true>(w_f32, p, s);
 }
 
+// Plain rows over several chunks, with or without the next-row tile.
 template <int LPR, int V, int U>
 static hipError_t bwd_dispatch(bool w_f32, const BwdParams& p, hipStream_t s)
 {
-    if (p.dres) return bwd_w<LPR, V, U, true, false>(w_f32, p, s);
     if (p.g) return bwd_gated<LPR, V, U>(w_f32, p, s);
-    return bwd_w<LPR, V, U, false, false>(w_f32, p, s);
+    if (p.dres)
+        return p.prefetch ? bwd_w<LPR, V, U, true, false, true>(w_f32, p, s) : bwd_w<LPR, V, U, true, false>(w_f32, p, s);
+    return p.prefetch ? bwd_w<LPR, V, U, false, false, true>(w_f32, p, s) : bwd_w<LPR, V, U, false, false>(w_f32, p, s);
 }
 
 // Single-workgroup path: the smallest U in {1, 2, 4} (up to direct_max_u)

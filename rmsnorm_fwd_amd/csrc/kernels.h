@@ -68,6 +68,7 @@ struct BwdParams {
     int col_vecs;         // column forms: 16-byte vectors per column slice (1, 2, 4 or 8)
     int slices;           // column forms: column slices, ceil(H / (8 col_vecs))
     int col_tasks;        // column forms: column tasks at the start of this launch's grid (0: row tasks only)
+    int prefetch;         // row kernel over several chunks, plain rows: 1 = next-row register tile
     double inv_h;
 };
 

@@ -24,6 +24,7 @@ size_t ws_bytes_for(int64_t R, int64_t H, const BwdRoute& r)
 bool route_valid(const BwdRoute& r, bool deterministic)
 {
     if (r.chunks < 1 || r.chunks > kMaxChunks) return false;
+    if (r.prefetch != 0 && r.prefetch != 1) return false;
     switch (r.form) {
     case FORM_PAIR:
         return r.col_chunks == 0 && r.col_vecs == 0;
@@ -31,6 +32,7 @@ bool route_valid(const BwdRoute& r, bool deterministic)
         return !deterministic && r.col_chunks == 0 && r.col_vecs == 0;
     case FORM_COLS:
     case FORM_COLS_TICKET: {
+        if (r.prefetch != 0) return false;
         if (r.form == FORM_COLS_TICKET && (deterministic || r.col_chunks < 2)) return false;
         const int v = r.col_vecs;
         return r.col_chunks >= 1 && r.col_chunks <= kMaxColChunks && (v == 1 || v == 2 || v == 4 || v == 8);
@@ -75,13 +77,64 @@ static int64_t cols_max_elems(int64_t H)
     return 8400000;
 }
 
+// The next-row tile of the row kernel (BwdRoute::prefetch), by width: the
+// largest row count that takes it on plain rows, the row count from which
+// it takes 512 workgroups instead of 256, and the same two for rows with
+// dres.  Measured on MI355X with cold caches (BF16 w, FP32 w at H 4096;
+// T 1024-131072): on plain rows the tile wins 2-11 % up to a few thousand
+// rows, where each compute unit holds one or two workgroups and no other
+// wavefront covers the load latency (T 4096, H 1536: 19.0 -> 17.8 us;
+// T 2048, H 5120: 28.1 -> 25.8 us; T 2048, H 4096: 24.0 -> 21.3 us), and
+// loses 1-10 % beyond, where it only adds registers (T 65536, H 4096:
+// 264 -> 283 us); it never wins at H 8192 and spills at H 16384.  With
+// dres, three loads per element, it wins at every row count measured from
+// H 1024 to 6144 (T 131072, H 6144: 1176 -> 1048 us; T 65536, H 4096:
+// 373 -> 351 us).  At H <= 128 it moved nothing beyond 1-3 %.  With dres a
+// route never takes more workgroups than without at the same row count, so
+// a workspace sized for plain rows also serves rows with dres.
+struct TileWindow {
+    int64_t max_h;       // serves H <= max_h (the smallest such entry)
+    int64_t rows;        // plain rows: the tile up to this many rows
+    int64_t wide_rows;   // ... with 512 workgroups from this many rows (else 256)
+    int64_t dres_rows;   // rows with dres: the tile up to this many rows
+    int64_t dres_wide;   // ... with 512 workgroups from this many rows
+};
+constexpr int64_t kAllRows = int64_t(1) << 40;
+static constexpr TileWindow kTileWindows[] = {
+    {128, 0, 0, 0, 0},
+    {512, 16384, kAllRows, 16384, kAllRows},
+    {1024, 8192, 6144, kAllRows, 6144},
+    {2048, 8192, kAllRows, kAllRows, kAllRows},
+    {3072, 8192, 6144, kAllRows, kAllRows},
+    {4096, 8192, kAllRows, kAllRows, kAllRows},
+    {5120, 16384, 4096, kAllRows, kAllRows},  // T 8192: 57.8 -> 56.0 us; T 16384: 96.4 -> 93.9 us
+    {6144, 4096, kAllRows, kAllRows, kAllRows},  // T 8192 even
+    {16384, 0, 0, 0, 0},
+};
+
+static const TileWindow& tile_window(int64_t H)
+{
+    int i = 0;
+    while (kTileWindows[i].max_h < H && kTileWindows[i].max_h < 16384) ++i;
+    return kTileWindows[i];
+}
+
 // The fixed-order pair's chunking for R rows of width H.
-BwdRoute pair_route(int64_t R, int64_t H)
+BwdRoute pair_route(int64_t R, int64_t H, bool residual, bool gated)
 {
     const int id = pick_layout(kBwdLayouts, kNumBwdLayouts, H);
     const Layout& L = kBwdLayouts[id < 0 ? 0 : id];
     const int64_t rpi = (int64_t)slots_of(L.lpr) * L.u;
     const int64_t groups = (R + rpi - 1) / rpi;
+    const TileWindow& tw = tile_window(H);
+    if (!gated && R <= (residual ? tw.dres_rows : tw.rows)) {
+        // with the tile, 256 workgroups (two or more iterations each, which
+        // the tile overlaps) beat 384 and 512 by 3-15 % at a few thousand
+        // rows, 512 where one row group is little work (H 1024) or many
+        // rows fall to each (H 3072 from 8192 rows)
+        const int64_t c = R >= (residual ? tw.dres_wide : tw.wide_rows) ? 512 : 256;
+        return BwdRoute{FORM_PAIR, (int)(c < groups ? c : groups), 0, 0, 1};
+    }
     // Measured on MI355X with cold caches, T*H from 2^23 to 2^30 elements,
     // both weight dtypes: the layout's chunk count (512 -- two workgroups per
     // compute unit -- for H <= 6144, 256 above) beats the other counts by
@@ -93,24 +146,25 @@ BwdRoute pair_route(int64_t R, int64_t H)
     // otherwise cost more than the rows themselves.  Measured at H 1536 to
     // 6144, T 256 to 2048: 4 rows per workgroup, but never fewer than 128
     // workgroups, is best or within 1.4 us of the best count.
-    // Up to R * H = 12 M elements 384 workgroups beat 512 (T 4096, H 1536:
-    // 18.8 against 19.6 us; T 2048, H 5120: 28.1 against 28.6 us, the same
-    // in two runs), above that 512 (T 6144, H 5120: 48.1 against 52.2 us).
     // Halving the partials' bytes with FP32 partials was slower at every
-    // size (19.6 -> 26.9 us; 263 -> 266 us at T 65536, H 4096).
+    // size (19.6 -> 26.9 us at T 4096, H 1536; 263 -> 266 us at T 65536,
+    // H 4096).
+    // The gated backward keeps the chunking it was measured with: up to
+    // R * H = 12 M elements 384 workgroups, the layout's count above.  Its
+    // rows load ahead by their own rule (one vector per lane) or not at all,
+    // and the tile window's 256 workgroups were slower for them at H 1536 -
+    // 4096 (T 8192, H 1536: 46 -> 67 us; T 4096, H 4096: 46 -> 56 us),
+    // faster only at H 6144 (T 2048: 47 -> 42 us).
     const int64_t per = (4 + rpi - 1) / rpi;  // row groups per workgroup
     int64_t c = (groups + per - 1) / per;
     if (c < 128) c = groups < 128 ? groups : 128;
-    const int64_t cap = R * H <= 12000000 && L.k > 384 ? 384 : L.k;
-    if (c > cap) c = cap;
-    return BwdRoute{FORM_PAIR, (int)(c > 0 ? c : 1), 0, 0};
+    if (gated && R * H <= 12000000 && c > 384) c = 384;
+    if (c > L.k) c = L.k;
+    return BwdRoute{FORM_PAIR, (int)(c > 0 ? c : 1), 0, 0, 0};
 }
 
-BwdRoute default_bwd_route(int64_t R, int64_t H, bool w_f32, bool residual, bool deterministic)
+static BwdRoute route_of(int64_t R, int64_t H, bool residual, bool gated)
 {
-    (void)w_f32;
-    (void)residual;
-    (void)deterministic;  // every routed form is deterministic: both modes take the same route
     const int id = pick_layout(kBwdLayouts, kNumBwdLayouts, H);
     const Layout& L = kBwdLayouts[id < 0 ? 0 : id];
     // column forms: row tasks take one row per row group, so a row group is
@@ -118,15 +172,37 @@ BwdRoute default_bwd_route(int64_t R, int64_t H, bool w_f32, bool residual, bool
     const int64_t cgroups = (R + slots_of(L.lpr) - 1) / slots_of(L.lpr);
     if (R <= cols1_max_rows(H)) {
         const int64_t c = cgroups < 1 ? 1 : cgroups;
-        return BwdRoute{FORM_COLS, (int)c, 1, cols1_vecs(R, H)};
+        return BwdRoute{FORM_COLS, (int)c, 1, cols1_vecs(R, H), 0};
     }
     if (R * H <= cols_max_elems(H)) {
         const int64_t c = cgroups < 512 ? cgroups : 512;
         int64_t cc = (12288 + H / 2) / H;
         if (cc < 2) cc = 2;
-        return BwdRoute{FORM_COLS, (int)c, (int)cc, 8};
+        return BwdRoute{FORM_COLS, (int)c, (int)cc, 8, 0};
     }
-    return pair_route(R, H);
+    return pair_route(R, H, residual, gated);
+}
+
+BwdRoute default_bwd_route(int64_t R, int64_t H, bool w_f32, bool residual, bool deterministic)
+{
+    (void)w_f32;
+    (void)deterministic;  // every routed form is deterministic: both modes take the same route
+    return route_of(R, H, residual, false);
+}
+
+BwdRoute gated_bwd_route(int64_t R, int64_t H, bool w_f32, bool deterministic)
+{
+    (void)w_f32;
+    (void)deterministic;
+    return route_of(R, H, false, true);
+}
+
+size_t bwd_workspace_bytes(int64_t R, int64_t H, bool w_f32, bool residual, bool deterministic)
+{
+    const size_t a = ws_bytes_for(R, H, default_bwd_route(R, H, w_f32, residual, deterministic));
+    if (residual) return a;
+    const size_t b = ws_bytes_for(R, H, gated_bwd_route(R, H, w_f32, deterministic));
+    return a > b ? a : b;
 }
 
 }  // namespace rmsn

@@ -31,6 +31,8 @@ struct BwdRoute {
     int chunks;      // workgroups that walk the rows (row kernel, or row tasks of the column forms)
     int col_chunks;  // column forms: row blocks per column slice (1: one pass over all rows)
     int col_vecs;    // column forms: 16-byte vectors (8 columns each) per column slice: 1, 2, 4 or 8
+    int prefetch;    // pair and atomic forms: 1 = the row kernel loads a workgroup's next rows while
+                     // it reduces the current ones (plain rows; no effect on any result bit)
 };
 
 // Workspace layout (bytes, every part 256-aligned):
@@ -53,11 +55,17 @@ size_t ws_bytes_for(int64_t R, int64_t H, const BwdRoute& r);
 // Column slices of a column form: ceil(H / (8 * col_vecs)).
 inline int64_t col_slices(int64_t H, int col_vecs) { return (H + 8 * col_vecs - 1) / (8 * col_vecs); }
 
-// The measured route table (route.cpp).
+// The measured route table (route.cpp): the plain backward's (residual:
+// rows with dres) and the SiLU-gated backward's.
 BwdRoute default_bwd_route(int64_t R, int64_t H, bool w_f32, bool residual, bool deterministic);
+BwdRoute gated_bwd_route(int64_t R, int64_t H, bool w_f32, bool deterministic);
 
-// The pair's chunking alone.
-BwdRoute pair_route(int64_t R, int64_t H);
+// The pair's chunking and next-row tile alone.
+BwdRoute pair_route(int64_t R, int64_t H, bool residual, bool gated);
+
+// Workspace bytes the size query reports: the plain route's, and without
+// dres at least the gated route's too (one size serves both backwards).
+size_t bwd_workspace_bytes(int64_t R, int64_t H, bool w_f32, bool residual, bool deterministic);
 
 // Largest chunk count a route may ask for, and largest row-block count per
 // column slice.

@@ -283,7 +283,8 @@ static void check_backward_shape(int64_t T, int64_t heads, int64_t H)
                       (long long)H);
                 rmsn_route rt{};
                 CHECK(rmsnorm_bwd_route(T, heads, H, wd, res, det, &rt) == RMSN_OK, "route query");
-                CHECK(ws == rmsnorm_bwd_workspace_size_for_route(T, heads, H, rt), "size of the route");
+                const size_t own = rmsnorm_bwd_workspace_size_for_route(T, heads, H, rt);
+                CHECK(ws >= own && (res == 0 || ws == own), "size of the route");
                 CHECK(!det || rt.form == RMSN_FORM_PAIR || rt.form == RMSN_FORM_COLS, "deterministic route form");
                 reset();
                 const int64_t sh = H, st = heads * sh;
@@ -297,7 +298,9 @@ static void check_backward_shape(int64_t T, int64_t heads, int64_t H)
                 CHECK(g.cols == 0 || (g.cols_rows == 1 && p.col_tasks == p.slices * p.col_chunks),
                       "one column-form launch holds the column and the row tasks");
                 CHECK(p.chunks >= 1 && p.chunks <= kMaxChunks, "chunks %d", p.chunks);
-                CHECK(p.form == rt.form && p.chunks == rt.chunks, "launch follows the route");
+                CHECK(p.form == rt.form && p.chunks == rt.chunks && p.prefetch == rt.prefetch,
+                      "launch follows the route");
+                CHECK(rt.prefetch == 0 || rt.prefetch == 1, "prefetch flag");
                 check_ws_accesses((const char*)P(6), ws, H, p.form, "rmsnorm_bwd");
                 if (p.form == FORM_PAIR && p.chunks > 1)
                     CHECK(!p.direct_dw && g.reduce == 1 && g.reduce_chunks == p.chunks && g.reduce_h == H,
@@ -326,13 +329,27 @@ static void check_backward_shape(int64_t T, int64_t heads, int64_t H)
                 reset();
                 const int sn = rmsnorm_bwd_noalloc(P(0), P(1), (const float*)P(2), P(3), wd, dres, P(4), (float*)P(5),
                                                    T, heads, H, st, sh, det, nullptr);
-                if (ws <= kScratchBytes) {
+                if (own <= kScratchBytes) {
                     CHECK(sn == RMSN_OK && g.scratch == 1 && g.bwd + g.cols == 1 && g.bp.form == rt.form &&
                               g.bp.chunks == rt.chunks && (const char*)g.bp.ticket == fake_scratch,
                           "noalloc runs the route on the scratch (status %d)", sn);
                 } else {
                     CHECK(sn == RMSN_ERR_WORKSPACE && g.bwd + g.cols == 0 && g.scratch == 0,
                           "noalloc refuses a route beyond the scratch");
+                }
+                // the size query without dres also serves the gated backward
+                if (res == 0) {
+                    reset();
+                    const int sg = rmsnorm_gated_bwd(P(0), P(1), P(8), (const float*)P(2), P(3), wd, P(4), P(7),
+                                                     (float*)P(5), P(6), ws, T, heads, H, st, sh, det, nullptr);
+                    rmsn_route gr{};
+                    CHECK(rmsnorm_gated_bwd_route(T, heads, H, wd, det, &gr) == RMSN_OK && gr.prefetch == 0 &&
+                              rmsnorm_bwd_workspace_size_for_route(T, heads, H, gr) <= ws,
+                          "gated route query");
+                    CHECK(sg == RMSN_OK && g.bwd + g.cols >= 1 && g.bp.prefetch == 0 && g.bp.form == gr.form &&
+                              g.bp.chunks == gr.chunks,
+                          "gated backward on the size query's workspace follows its route (status %d)", sg);
+                    check_ws_accesses((const char*)P(6), ws, H, g.bp.form, "gated");
                 }
             }
 }
@@ -399,9 +416,31 @@ static void check_gated_forward_table()
     }
 }
 
+// Explicit row-kernel routes with and without the next-row tile: the flag
+// reaches the launch; a column form refuses it.
+static void check_prefetch_routes()
+{
+    const int64_t T = 4099, H = 1536;
+    for (int form : {RMSN_FORM_PAIR, RMSN_FORM_ATOMIC})
+        for (int pf : {0, 1}) {
+            const rmsn_route r{form, 256, 0, 0, pf};
+            const size_t ws = rmsnorm_bwd_workspace_size_for_route(T, 1, H, r);
+            reset();
+            const int st = rmsnorm_bwd_routed(P(0), P(1), (const float*)P(2), P(3), RMSN_W_BF16, nullptr, P(4),
+                                              (float*)P(5), P(6), ws, T, 1, H, H, H, form == RMSN_FORM_PAIR, r, nullptr);
+            CHECK(st == RMSN_OK && g.bwd == 1 && g.bp.prefetch == pf && g.bp.chunks == 256, "prefetch route launch");
+        }
+    const rmsn_route bad{RMSN_FORM_COLS, 8, 2, 8, 1};
+    CHECK(rmsnorm_bwd_workspace_size_for_route(T, 1, H, bad) == 0, "column form with prefetch has no size");
+    CHECK(rmsnorm_bwd_routed(P(0), P(1), (const float*)P(2), P(3), RMSN_W_BF16, nullptr, P(4), (float*)P(5), P(6),
+                             size_t(1) << 30, T, 1, H, H, H, 1, bad, nullptr) == RMSN_ERR_INVALID_ARG,
+          "column form refuses prefetch");
+}
+
 int main()
 {
     check_error_paths();
+    check_prefetch_routes();
     check_gated_forward_table();
     const int64_t Ts[] = {1, 2, 3, 4, 5, 7, 16, 63, 64, 65, 255, 256, 257, 1000, 1024, 4096, 4099,
                           16384, 32767, 32768, 65535, 65536, 131072, 1 << 20, (int64_t(1) << 30) - 1};

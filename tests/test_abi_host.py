@@ -108,7 +108,8 @@ def test_bwd_rejects_bad_arguments(kw, status):
 
 
 def test_workspace_size_follows_the_route():
-    # the size is that of the route rmsnorm_bwd takes for the same arguments,
+    # the size is that of the route rmsnorm_bwd takes for the same arguments
+    # (without dres at least that: it covers the gated backward's route too),
     # a pure function of them, never below the prepared part, and 0 for
     # invalid shapes or weight dtypes
     for (T, heads, H) in [(4096, 1, 1536), (65536, 1, 4096), (131072, 1, 6144), (32768, 24, 256),
@@ -119,7 +120,8 @@ def test_workspace_size_follows_the_route():
                     a = rn.rmsnorm_bwd_workspace_size(T, heads, H, wd, res, det)
                     assert a == rn.rmsnorm_bwd_workspace_size(T, heads, H, wd, res, det)
                     route = rn.rmsnorm_bwd_route(T, heads, H, wd, res, det)
-                    assert a == rn.rmsnorm_bwd_workspace_size_for_route(T, heads, H, route) > 0
+                    own = rn.rmsnorm_bwd_workspace_size_for_route(T, heads, H, route)
+                    assert a >= own > 0 and (a == own or not res)
                     assert a >= prepared_bytes(H)
                     if det:
                         assert route[0] in (rn.RMSN_FORM_PAIR, rn.RMSN_FORM_COLS)
@@ -157,6 +159,9 @@ def _routed(route, det=1, T=4, H=64):
     ((rn.RMSN_FORM_COLS, 8, 1, 16), 1),         # slice wider than 8 vectors
     ((rn.RMSN_FORM_COLS_TICKET, 8, 4, 8), 1),   # tickets need the prepared workspace
     ((rn.RMSN_FORM_COLS_TICKET, 8, 1, 8), 0),   # a ticket needs two row blocks at least
+    ((rn.RMSN_FORM_PAIR, 8, 0, 0, 2), 1),       # prefetch is 0 or 1
+    ((rn.RMSN_FORM_PAIR, 8, 0, 0, -1), 1),
+    ((rn.RMSN_FORM_COLS, 8, 2, 8, 1), 1),       # no next-row tile in the column forms
 ])
 def test_routed_rejects_malformed_routes(route, det):
     assert _routed(route, det) == rn.RMSN_ERR_INVALID_ARG
@@ -245,22 +250,30 @@ def test_oracle_under_sanitizers(tmp_path):
 def test_route_table_moves_from_column_forms_to_the_pair():
     # as rows grow: the one-pass column form (one launch, no partials), then
     # the two-launch column form, then the fixed-order pair; never back.  Both
-    # modes take the same route (every routed form is deterministic); chunk
-    # counts stay within their bounds
+    # modes and both weight dtypes take the same route (every routed form is
+    # deterministic); with dres the same form, never more workgroups (so a
+    # workspace sized without dres serves it) and the next-row tile wherever
+    # plain rows take it; chunk counts stay within their bounds
     order = {(rn.RMSN_FORM_COLS, True): 0, (rn.RMSN_FORM_COLS, False): 1, (rn.RMSN_FORM_PAIR, False): 2}
     for H in (256, 512, 1536, 2048, 4096, 5120, 6144, 8192, 16384):
         prev = 0
-        for T in [1, 2, 3, 4, 7, 16, 64, 100, 256, 384, 449, 512, 768, 1024, 2048, 4096, 16384, 65536, 131072]:
+        for T in [1, 2, 3, 4, 7, 16, 64, 100, 256, 384, 449, 512, 768, 1024, 2048, 4096, 6143, 6144, 8192, 8193,
+                  16384, 16385, 65536, 131072]:
             r = rn.rmsnorm_bwd_route(T, 1, H, 0, 0, 1)
-            assert r == rn.rmsnorm_bwd_route(T, 1, H, 1, 1, 0)
-            form, chunks, cc, cv = r
+            assert r == rn.rmsnorm_bwd_route(T, 1, H, 1, 0, 0)
+            rr = rn.rmsnorm_bwd_route(T, 1, H, 0, 1, 1)
+            assert rr == rn.rmsnorm_bwd_route(T, 1, H, 1, 1, 0)
+            assert rr[0] == r[0] and rr[1] <= r[1] and rr[4] >= r[4], (H, T, r, rr)
+            assert rn.rmsnorm_bwd_workspace_size(T, 1, H, 0, True) <= rn.rmsnorm_bwd_workspace_size(T, 1, H, 0, False)
+            form, chunks, cc, cv, pf = r
             stage = order[(form, cc == 1)]
             assert stage >= prev, (H, T, r)
             prev = stage
             if form == rn.RMSN_FORM_PAIR:
-                assert 1 <= chunks <= 512 and cc == cv == 0
+                assert 1 <= chunks <= 512 and cc == cv == 0 and pf in (0, 1)
             else:
                 assert 1 <= chunks <= min(T, 512 if cc > 1 else T) and cv in (1, 2, 4, 8) and 1 <= cc <= 64
+                assert pf == 0
         assert rn.rmsnorm_bwd_route(1, 1, H, 0, 0, 1)[:3] == (rn.RMSN_FORM_COLS, 1, 1)
         assert prev == 2 and rn.rmsnorm_bwd_route(65536, 1, H, 0, 0, 1)[1] >= 256
 

@@ -261,3 +261,22 @@ def test_gated_full_size_headline_shape():
     dx3, dg3, dw3 = rn.rmsnorm_gated_bwd(DY, X, G, rstd, W, deterministic=False)
     assert torch.equal(dx3, dx) and torch.equal(dg3, dg)
     assert (np.abs(dw3.cpu().numpy().astype(np.float64) - ref_dw) <= bw).all()
+
+
+@pytest.mark.parametrize("H", [1536, 4096, 6144])
+def test_gated_route_edges_from_both_sides(H):
+    # each change of the gated backward's form (one-pass column form ->
+    # two-launch column form -> pair) is run on both sides against the oracle
+    import rmsnorm_fwd_amd as rn
+    edges, prev = [], rn.rmsnorm_gated_bwd_route(1, 1, H, 0, 1)
+    for T in range(2, 8192):
+        r = rn.rmsnorm_gated_bwd_route(T, 1, H, 0, 1)
+        assert r[4] == 0
+        if r[0] != prev[0] or (r[2] == 1) != (prev[2] == 1):
+            edges.append(T)
+        prev = r
+    assert len(edges) >= 1
+    for T in edges:
+        for t in (T - 1, T):
+            print(H, t, run_gated(Layout.plain(t, H), "bf16", seed=t))
+

@@ -210,30 +210,62 @@ def test_column_form_dw_is_the_same_with_and_without_tickets(T, H):
     assert int(ws[:prepared_bytes(H)].count_nonzero()) == 0
 
 
-def _route_edges(heads, H, t_max):
-    """Token counts T where the default route differs from T - 1's."""
+def _route_edges(heads, H, t_max, res=False):
+    """Token counts T where the default route's form, one-pass column form or
+    next-row tile differs from T - 1's."""
     import rmsnorm_fwd_amd as rn
-    edges, prev = [], rn.rmsnorm_bwd_route(1, heads, H, 0, 0, 1)
+    edges, prev = [], rn.rmsnorm_bwd_route(1, heads, H, 0, res, 1)
     for T in range(2, t_max + 1):
-        r = rn.rmsnorm_bwd_route(T, heads, H, 0, 0, 1)
-        if r[0] != prev[0] or (r[2] == 1) != (prev[2] == 1):
+        r = rn.rmsnorm_bwd_route(T, heads, H, 0, res, 1)
+        if r[0] != prev[0] or (r[2] == 1) != (prev[2] == 1) or r[4] != prev[4]:
             edges.append(T)
         prev = r
     return edges
 
 
-@pytest.mark.parametrize("heads,H", [(4, 256), (1, 1536), (1, 4096), (1, 6144), (1, 8192)])
-def test_route_edges_from_both_sides(heads, H):
+@pytest.mark.parametrize("heads,H,res", [(4, 256, False), (1, 1536, False), (1, 4096, False), (1, 6144, False),
+                                         (1, 8192, False), (1, 1024, True), (1, 5120, True)])
+def test_route_edges_from_both_sides(heads, H, res):
     # each change of backward form (one-pass column form -> two-launch column
-    # form -> pair) is run on both sides, in both modes, against the oracle
-    # (p3 commit message: each new edge is exercised from both sides)
-    edges = _route_edges(heads, H, 16384 // heads + 64)
+    # form -> pair, with then without the next-row tile) is run on both
+    # sides, in both modes, against the oracle (p3 commit message: each new
+    # edge is exercised from both sides)
+    edges = _route_edges(heads, H, 16384 // heads + 64, res)
     assert len(edges) >= 1
     for T in edges:
         for t in (T - 1, T):
             L = Layout.heads_view(t, heads, H, heads * H, H) if heads > 1 else Layout.plain(t, H)
-            rep = run_case(L, "bf16", seed=t, det_repeats=2)
-            print(heads, H, t, rep)
+            rep = run_case(L, "bf16", res=res, dres=res, seed=t, det_repeats=2)
+            print(heads, H, res, t, rep)
+
+
+@pytest.mark.parametrize("H", [64, 256, 512, 1024, 1536, 2048, 3072, 4096, 6144, 8192, 16384])
+@pytest.mark.parametrize("dres,wdt", [(False, "bf16"), (True, "bf16"), (False, "f32")])
+def test_next_row_tile_changes_no_bit(H, dres, wdt):
+    """The row kernel with and without the next-row tile, at the same chunk
+    counts (a row group per workgroup, several iterations each, a ragged last
+    iteration), with and without dres: dx and the deterministic dw bit for bit
+    the same, and within budget of the oracle."""
+    import torch
+    import rmsnorm_fwd_amd as rn
+    from tests.helpers import gen_case, to_dev_bf16, weight_dev
+    T = 1000 if H <= 2048 else 301
+    x, _, dy, dr, w = gen_case(61 + H, Layout.plain(T, H), wdt, False, dres)
+    X, DY, W = to_dev_bf16(x).view(T, H), to_dev_bf16(dy).view(T, H), weight_dev(w)
+    DR = to_dev_bf16(dr).view(T, H) if dres else None
+    _, rstd, _ = rn.rmsnorm_fwd(X, W)
+    for chunks in (3, 37, 256, 1000):
+        got = [rn.rmsnorm_bwd_routed(DY, X, rstd, W, (0, chunks, 0, 0, pf), residual=DR, deterministic=True)
+               for pf in (0, 1, 1)]
+        torch.cuda.synchronize()
+        for dx, dw in got[1:]:
+            assert torch.equal(dx, got[0][0]) and torch.equal(dw, got[0][1]), (H, chunks)
+        nd = rn.rmsnorm_bwd_routed(DY, X, rstd, W, (1, chunks, 0, 0, 1), residual=DR, deterministic=False)
+        torch.cuda.synchronize()
+        assert torch.equal(nd[0], got[0][0])
+    rep = run_case(Layout.plain(T, H), wdt, res=dres, dres=dres, seed=61 + H,
+                   routes=[(0, 256, 0, 0, 1), (0, 37, 0, 0, 1), (1, 64, 0, 0, 1)])
+    print(H, dres, wdt, rep)
 
 
 def test_deterministic_dw_repeats_at_scale():
