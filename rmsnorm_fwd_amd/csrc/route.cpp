@@ -147,8 +147,9 @@ BwdRoute pair_route(int64_t R, int64_t H, bool residual, bool gated)
     // 6144, T 256 to 2048: 4 rows per workgroup, but never fewer than 128
     // workgroups, is best or within 1.4 us of the best count.
     // Halving the partials' bytes with FP32 partials was slower at every
-    // size (19.6 -> 26.9 us at T 4096, H 1536; 263 -> 266 us at T 65536,
-    // H 4096).
+    // size, measured twice (with the next-row tile: 18.1 -> 21.8 us at
+    // T 4096, H 1536, 26.3 with 32-column reduce workgroups; 265 -> 269 us
+    // at T 65536, H 4096).
     // The gated backward keeps the chunking it was measured with: up to
     // R * H = 12 M elements 384 workgroups, the layout's count above.  Its
     // rows load ahead by their own rule (one vector per lane) or not at all,
