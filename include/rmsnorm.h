@@ -222,8 +222,9 @@ int rmsnorm_gated_bwd(const void* dy, const void* x, const void* gate, const flo
  *          its next rows while it reduces the current ones (a second
  *          register tile; pays where a compute unit holds few workgroups);
  *          0 or 1, and 0 for the column forms.  A scheduling choice only: it
- *          changes no bit of dx or dw.  It has no effect with chunks = 1 or
- *          on the gated backward, whose rows of one vector per lane always
+ *          changes no bit of dx or dw.  It has no effect with chunks = 1,
+ *          on rows wider than 8192 (no registers for a second tile) or on
+ *          the gated backward, whose rows of one vector per lane always
  *          load ahead.
  * The per-row work, and so dx, does not depend on the route.
  */

@@ -173,19 +173,47 @@ __device__ __forceinline__ void bwd_rows(const BwdParams& p, int chunk, int nchu
     if constexpr (PF) {
         if (first < row1) bwd_load<U, V, SLOTS, DRES, GATE>(cur, p, lv, first, slot, row1);
     }
-    double w64[V][8];
+    // The weights in FP64 registers, 0 for vectors a lane does not own; rows
+    // wider than 8192 (four or more vectors per lane) keep them as loaded
+    // and widen each one where it is used, since FP64 copies would not fit
+    // the registers a lane has beside its column sums.
+    constexpr bool WRAW = LPR * V * 8 > 8192;
+    double w64[WRAW ? 1 : V][8];
 #pragma unroll
     for (int v = 0; v < V; ++v) {
-        float wv[8];
-        if constexpr (WF32) {
-            wv[0] = wa[v].x; wv[1] = wa[v].y; wv[2] = wa[v].z; wv[3] = wa[v].w;
-            wv[4] = wb[v].x; wv[5] = wb[v].y; wv[6] = wb[v].z; wv[7] = wb[v].w;
+        if constexpr (WRAW) {
+            if (!lv.ok[v]) wa[v] = wb[WF32 ? v : 0] = make_float4(0.f, 0.f, 0.f, 0.f);
         } else {
-            unpack8(*reinterpret_cast<const uint4*>(&wa[v]), wv);
-        }
+            float wv[8];
+            if constexpr (WF32) {
+                wv[0] = wa[v].x; wv[1] = wa[v].y; wv[2] = wa[v].z; wv[3] = wa[v].w;
+                wv[4] = wb[v].x; wv[5] = wb[v].y; wv[6] = wb[v].z; wv[7] = wb[v].w;
+            } else {
+                unpack8(*reinterpret_cast<const uint4*>(&wa[v]), wv);
+            }
 #pragma unroll
-        for (int e = 0; e < 8; ++e) w64[v][e] = lv.ok[v] ? (double)wv[e] : 0.0;
+            for (int e = 0; e < 8; ++e) w64[v][e] = lv.ok[v] ? (double)wv[e] : 0.0;
+        }
     }
+    // weight e of vector v, as FP32 (exact for BF16 and FP32 weights)
+    auto wf32 = [&](int v, int e) -> float {
+        if constexpr (!WRAW) {
+            return (float)w64[v][e];
+        } else if constexpr (WF32) {
+            const float4& q = e < 4 ? wa[v] : wb[v];
+            const int k = e & 3;
+            return k == 0 ? q.x : k == 1 ? q.y : k == 2 ? q.z : q.w;
+        } else {
+            const float4& q = wa[v];
+            const int k = e >> 1;
+            const unsigned word = __float_as_uint(k == 0 ? q.x : k == 1 ? q.y : k == 2 ? q.z : q.w);
+            return __uint_as_float((e & 1) ? (word & 0xffff0000u) : (word << 16));
+        }
+    };
+    auto wf64 = [&](int v, int e) -> double {
+        if constexpr (WRAW) return (double)wf32(v, e);
+        else return w64[v][e];
+    };
     int it = 0;
     for (int base = first; base < row1; base += step, ++it) {
         if constexpr (PF) {
@@ -221,11 +249,27 @@ __device__ __forceinline__ void bwd_rows(const BwdParams& p, int chunk, int nchu
                     // own error bound) before it joins the FP64 sums.
                     double pd = GATE ? (double)((xf[e] * df[e]) * sg[e]) : (double)(xf[e] * df[e]);
                     if constexpr (DW) acc[v][e] = __builtin_fma(pd, rho[u], acc[v][e]);
-                    S[u] = __builtin_fma(pd, w64[v][e], S[u]);
+                    S[u] = __builtin_fma(pd, wf64(v, e), S[u]);
                 }
             }
         }
         row_group_sum<LPR, U, RPI>(S, red, it, slot, g);
+        if constexpr (WRAW || (GATE && LPR >= 1024)) {
+            // Wide rows: unpack the tile again in the second pass rather
+            // than hold the first pass's FP32 values across the row
+            // reduction (an empty asm hides that they are unchanged; it
+            // emits no instruction).
+#pragma unroll
+            for (int u = 0; u < U; ++u)
+#pragma unroll
+                for (int v = 0; v < V; ++v) {
+                    asm volatile("" : "+v"(xv[u][v].x), "+v"(xv[u][v].y), "+v"(xv[u][v].z), "+v"(xv[u][v].w));
+                    asm volatile("" : "+v"(dv[u][v].x), "+v"(dv[u][v].y), "+v"(dv[u][v].z), "+v"(dv[u][v].w));
+                    if constexpr (DRES || GATE)
+                        asm volatile("" : "+v"(cur.rv[u][v].x), "+v"(cur.rv[u][v].y), "+v"(cur.rv[u][v].z),
+                                     "+v"(cur.rv[u][v].w));
+                }
+        }
 #pragma unroll
         for (int u = 0; u < U; ++u) {
             const double L = rho[u] * rho[u] * rho[u] * S[u] * p.inv_h;
@@ -247,7 +291,7 @@ __device__ __forceinline__ void bwd_rows(const BwdParams& p, int chunk, int nchu
                     float d[8], q[8];
 #pragma unroll
                     for (int e = 0; e < 8; ++e) {
-                        const float wf = (float)w64[v][e];  // exact: w is BF16 or FP32
+                        const float wf = wf32(v, e);
                         const float sgm = sigmoid_f32(rf[e]);
                         const float dsilu = sgm * __builtin_fmaf(rf[e], 1.0f - sgm, 1.0f);
                         const float ef = df[e] * (rf[e] * sgm);
@@ -260,7 +304,7 @@ __device__ __forceinline__ void bwd_rows(const BwdParams& p, int chunk, int nchu
                     double d[8];
 #pragma unroll
                     for (int e = 0; e < 8; ++e) {
-                        const double gw = w64[v][e] * (double)df[e];  // exact
+                        const double gw = wf64(v, e) * (double)df[e];  // exact
                         d[e] = __builtin_fma(gw, rho[u], -((double)xf[e] * L));
                         if constexpr (DRES) d[e] += (double)rf[e];
                     }
@@ -568,21 +612,35 @@ constexpr int gated_u() { return LPR <= 256 ? 1 : U; }
 // gives them the double-buffered loads of one-vector gated rows.  Rows of
 // two vectors stay as they are: as rows of twice the lanes they ran 1.2-1.4x
 // slower, and the second tile does not fit their registers.
+// Gated rows of 1024 lanes x 1 vector (H 8192) have the 128 registers of
+// four wavefronts per SIMD and spill; they run as 512 lanes x 2 vectors.
+template <int LPR, int V>
+constexpr bool gated_halve_lanes() { return LPR == 1024 && V == 1; }
+
 template <int LPR, int V, int U>
 static hipError_t bwd_gated(bool w_f32, const BwdParams& p, hipStream_t s)
 {
     if constexpr (RMSN_GATED_WIDE_V3 && V == 3 && LPR <= 256) return bwd_w<3 * LPR, 1, 1, false, true>(w_f32, p, s);
+    else if constexpr (gated_halve_lanes<LPR, V>()) return bwd_w<LPR / 2, 2 * V, 1, false, true>(w_f32, p, s);
     else return bwd_w<LPR, V, gated_u<LPR, V, U>(), false, true>(w_f32, p, s);
 }
 
-// Plain rows over several chunks, with or without the next-row tile.
+// Plain rows over several chunks, with or without the next-row tile (rows
+// wider than 8192 have no registers for a second tile and ignore it).
 template <int LPR, int V, int U>
 static hipError_t bwd_dispatch(bool w_f32, const BwdParams& p, hipStream_t s)
 {
     if (p.g) return bwd_gated<LPR, V, U>(w_f32, p, s);
-    if (p.dres)
-        return p.prefetch ? bwd_w<LPR, V, U, true, false, true>(w_f32, p, s) : bwd_w<LPR, V, U, true, false>(w_f32, p, s);
-    return p.prefetch ? bwd_w<LPR, V, U, false, false, true>(w_f32, p, s) : bwd_w<LPR, V, U, false, false>(w_f32, p, s);
+    if constexpr (LPR * V * 8 > 8192) {
+        if (p.dres) return bwd_w<LPR, V, U, true, false>(w_f32, p, s);
+        return bwd_w<LPR, V, U, false, false>(w_f32, p, s);
+    } else {
+        if (p.dres)
+            return p.prefetch ? bwd_w<LPR, V, U, true, false, true>(w_f32, p, s)
+                              : bwd_w<LPR, V, U, true, false>(w_f32, p, s);
+        return p.prefetch ? bwd_w<LPR, V, U, false, false, true>(w_f32, p, s)
+                          : bwd_w<LPR, V, U, false, false>(w_f32, p, s);
+    }
 }
 
 // Single-workgroup path: the smallest U in {1, 2, 4} (up to direct_max_u)
@@ -647,6 +705,7 @@ static hipError_t bwd_cols_dispatch(bool w_f32, const BwdParams& p, bool rows, h
     if (p.g) {
         if constexpr (RMSN_GATED_WIDE_V3 && V == 3 && LPR <= 256)
             return bwd_cols_w<3 * LPR, 1, false, true>(w_f32, p, rows, s);
+        else if constexpr (gated_halve_lanes<LPR, V>()) return bwd_cols_w<LPR / 2, 2 * V, false, true>(w_f32, p, rows, s);
         else return bwd_cols_w<LPR, V, false, true>(w_f32, p, rows, s);
     }
     return bwd_cols_w<LPR, V, false, false>(w_f32, p, rows, s);
