@@ -49,6 +49,7 @@
 // bound silu's error sets (the tolerance the tests derive).
 #include <atomic>
 #include <mutex>
+#include <type_traits>
 
 #include "../../include/rmsnorm.h"
 #include "device_common.h"
@@ -85,17 +86,27 @@ __device__ __forceinline__ double chunk_group_sum(const double* part, int chunks
 // One iteration's rows of a row group: addresses, rstd and the x / dy (and
 // dres, or the gate g) vectors, all loaded before any of them is used.
 // DRES and GATE never meet.
-template <int U, int V, bool DRES, bool GATE>
+//
+// rstd: with DEFER it is loaded unconditionally (rr is in range) and widened
+// and masked only where it is used, so nothing in the load waits and the
+// row's other loads go out behind it at once; without, it is masked and
+// widened as it arrives, and that wait also drains the wavefront's earlier
+// stores before the row's loads go out.  The second is faster for rows that
+// stream at full occupancy (each wavefront's reads and writes stay in
+// separate phases: T 131072, H 6144: 738 against 865 us), the first where
+// few wavefronts share a compute unit and the next-row tile is in use
+// (T 4096, H 1536: 18.0 -> 16.8 us; gated T 16384, H 3072: 169 -> 110 us).
+template <int U, int V, bool DRES, bool GATE, bool DEFER>
 struct BwdTile {
     bool ok[U];
     int64_t off[U];
-    double rho[U];
+    typename std::conditional<DEFER, float, double>::type rho[U];
     uint4 xv[U][V], dv[U][V];
     uint4 rv[(DRES || GATE) ? U : 1][(DRES || GATE) ? V : 1];
 };
 
-template <int U, int V, int SLOTS, bool DRES, bool GATE>
-__device__ __forceinline__ void bwd_load(BwdTile<U, V, DRES, GATE>& t, const BwdParams& p,
+template <int U, int V, int SLOTS, bool DRES, bool GATE, bool DEFER>
+__device__ __forceinline__ void bwd_load(BwdTile<U, V, DRES, GATE, DEFER>& t, const BwdParams& p,
                                          const LaneVectors<V>& lv, int base, int slot, int row1)
 {
 #pragma unroll
@@ -104,7 +115,8 @@ __device__ __forceinline__ void bwd_load(BwdTile<U, V, DRES, GATE>& t, const Bwd
         t.ok[u] = row < row1;
         const int rr = t.ok[u] ? row : row1 - 1;  // rows past the end re-read the last row
         t.off[u] = row_offset(rr, p.rows);
-        t.rho[u] = t.ok[u] ? (double)p.rstd[rr] : 0.0;  // ... and add nothing to dw
+        if constexpr (DEFER) t.rho[u] = p.rstd[rr];
+        else t.rho[u] = t.ok[u] ? (double)p.rstd[rr] : 0.0;  // ... and add nothing to dw
     }
 #pragma unroll
     for (int u = 0; u < U; ++u)
@@ -168,10 +180,12 @@ __device__ __forceinline__ void bwd_rows(const BwdParams& p, int chunk, int nchu
     // Plain rows do when the route asks (PFP): where each compute unit holds
     // few workgroups, as at a few thousand rows.  Results do not depend on it.
     constexpr bool PF = GATE ? V == 1 : PFP;
-    BwdTile<U, V, DRES, GATE> cur;
-    BwdTile<PF ? U : 1, PF ? V : 1, DRES, GATE> nxt;
+    constexpr bool DEFER = PF && !DRES;  // see BwdTile
+    using Tile = BwdTile<U, V, DRES, GATE, DEFER>;
+    Tile cur;
+    BwdTile<PF ? U : 1, PF ? V : 1, DRES, GATE, DEFER> nxt;
     if constexpr (PF) {
-        if (first < row1) bwd_load<U, V, SLOTS, DRES, GATE>(cur, p, lv, first, slot, row1);
+        if (first < row1) bwd_load<U, V, SLOTS, DRES, GATE, DEFER>(cur, p, lv, first, slot, row1);
     }
     // The weights in FP64 registers, 0 for vectors a lane does not own; rows
     // wider than 8192 (four or more vectors per lane) keep them as loaded
@@ -214,18 +228,22 @@ __device__ __forceinline__ void bwd_rows(const BwdParams& p, int chunk, int nchu
         if constexpr (WRAW) return (double)wf32(v, e);
         else return w64[v][e];
     };
-    int it = 0;
-    for (int base = first; base < row1; base += step, ++it) {
-        if constexpr (PF) {
-            if (base + step < row1) bwd_load<U, V, SLOTS, DRES, GATE>(nxt, p, lv, base + step, slot, row1);
+    // The work on one iteration's rows, already loaded into t.
+    auto work = [&](Tile& t, int it) {
+        const bool* ok = t.ok;
+        const int64_t* off = t.off;
+        // rstd in FP64; rows past the end add nothing to dw
+        double rho_d[DEFER ? U : 1];
+        const double* rho;
+        if constexpr (DEFER) {
+#pragma unroll
+            for (int u = 0; u < U; ++u) rho_d[u] = ok[u] ? (double)t.rho[u] : 0.0;
+            rho = rho_d;
         } else {
-            bwd_load<U, V, SLOTS, DRES, GATE>(cur, p, lv, base, slot, row1);
+            rho = t.rho;
         }
-        const bool* ok = cur.ok;
-        const int64_t* off = cur.off;
-        const double* rho = cur.rho;
-        uint4 (&xv)[U][V] = cur.xv;
-        uint4 (&dv)[U][V] = cur.dv;
+        uint4 (&xv)[U][V] = t.xv;
+        uint4 (&dv)[U][V] = t.dv;
         double S[U];
 #pragma unroll
         for (int u = 0; u < U; ++u) {
@@ -238,7 +256,7 @@ __device__ __forceinline__ void bwd_rows(const BwdParams& p, int chunk, int nchu
                 float sg[8];  // silu(g) with a gate, else unused
                 if constexpr (GATE) {
                     float gf[8];
-                    unpack8(cur.rv[u][v], gf);
+                    unpack8(t.rv[u][v], gf);
 #pragma unroll
                     for (int e = 0; e < 8; ++e) sg[e] = gf[e] * sigmoid_f32(gf[e]);
                 }
@@ -266,8 +284,8 @@ __device__ __forceinline__ void bwd_rows(const BwdParams& p, int chunk, int nchu
                     asm volatile("" : "+v"(xv[u][v].x), "+v"(xv[u][v].y), "+v"(xv[u][v].z), "+v"(xv[u][v].w));
                     asm volatile("" : "+v"(dv[u][v].x), "+v"(dv[u][v].y), "+v"(dv[u][v].z), "+v"(dv[u][v].w));
                     if constexpr (DRES || GATE)
-                        asm volatile("" : "+v"(cur.rv[u][v].x), "+v"(cur.rv[u][v].y), "+v"(cur.rv[u][v].z),
-                                     "+v"(cur.rv[u][v].w));
+                        asm volatile("" : "+v"(t.rv[u][v].x), "+v"(t.rv[u][v].y), "+v"(t.rv[u][v].z),
+                                     "+v"(t.rv[u][v].w));
                 }
         }
 #pragma unroll
@@ -278,7 +296,7 @@ __device__ __forceinline__ void bwd_rows(const BwdParams& p, int chunk, int nchu
                 float xf[8], df[8], rf[8];
                 unpack8(xv[u][v], xf);
                 unpack8(dv[u][v], df);
-                if constexpr (DRES || GATE) unpack8(cur.rv[u][v], rf);
+                if constexpr (DRES || GATE) unpack8(t.rv[u][v], rf);
                 uint4 o;
                 if constexpr (GATE) {
                     // The gated gradient e = dy * silu(g) carries silu's FP32
@@ -316,8 +334,35 @@ __device__ __forceinline__ void bwd_rows(const BwdParams& p, int chunk, int nchu
                 if (ok[u] && lv.ok[v]) st16_stream(p.dx + off[u] + lv.col[v], o);
             }
         }
-        if constexpr (PF) {
-            if (base + step < row1) cur = nxt;
+    };
+    if constexpr (DEFER) {
+        // The loop runs while a next iteration exists and loads it
+        // unconditionally, the last iteration after it: every path into the
+        // work then has the same loads in flight, so the wait before the
+        // work leaves the next rows' loads outstanding (with a conditional
+        // load the paths' waits merge into one that drains them all).
+        if (first < row1) {
+            int it = 0;
+            int base = first;
+            for (; base + step < row1; base += step, ++it) {
+                bwd_load<U, V, SLOTS, DRES, GATE, DEFER>(nxt, p, lv, base + step, slot, row1);
+                work(cur, it);
+                cur = nxt;
+            }
+            work(cur, it);
+        }
+    } else {
+        int it = 0;
+        for (int base = first; base < row1; base += step, ++it) {
+            if constexpr (PF) {
+                if (base + step < row1) bwd_load<U, V, SLOTS, DRES, GATE, DEFER>(nxt, p, lv, base + step, slot, row1);
+            } else {
+                bwd_load<U, V, SLOTS, DRES, GATE, DEFER>(cur, p, lv, base, slot, row1);
+            }
+            work(cur, it);
+            if constexpr (PF) {
+                if (base + step < row1) cur = nxt;
+            }
         }
     }
 }
