@@ -224,8 +224,7 @@ int rmsnorm_gated_bwd(const void* dy, const void* x, const void* gate, const flo
  *          0 or 1, and 0 for the column forms.  A scheduling choice only: it
  *          changes no bit of dx or dw.  It has no effect with chunks = 1,
  *          on rows wider than 8192 (no registers for a second tile) or on
- *          the gated backward, whose rows of one vector per lane always
- *          load ahead.
+ *          the gated backward, whose rows up to H 8192 always load ahead.
  * The per-row work, and so dx, does not depend on the route.
  */
 enum rmsn_form { RMSN_FORM_PAIR = 0, RMSN_FORM_ATOMIC = 1, RMSN_FORM_COLS = 2, RMSN_FORM_COLS_TICKET = 3 };
@@ -243,8 +242,9 @@ int rmsnorm_bwd_route(int64_t T, int64_t heads, int64_t H, int w_dtype, int has_
                       int deterministic, rmsn_route* out);
 
 /* The route rmsnorm_gated_bwd takes: the plain backward's forms, with the
- * pair's chunk counts measured for the gated rows (no next-row tile window;
- * prefetch is always 0).  Returns a status. */
+ * pair's chunk counts measured for the gated rows (which take the next-row
+ * tile by width, not by route: prefetch is always 0 here).  Returns a
+ * status. */
 int rmsnorm_gated_bwd_route(int64_t T, int64_t heads, int64_t H, int w_dtype, int deterministic,
                             rmsn_route* out);
 
@@ -268,9 +268,10 @@ int rmsnorm_bwd_routed(const void* dy, const void* x, const float* rstd, const v
  * own device scratch of RMSN_NOALLOC_SCRATCH_BYTES per GPU, set up on the
  * first call on a device (a symbol lookup, and a clear of its prepared part
  * enqueued on `stream`) and held until the process ends.  Allocates nothing,
- * ever.  Returns RMSN_ERR_WORKSPACE when the route's workspace
- * (rmsnorm_bwd_workspace_size) exceeds the scratch -- every width up to
- * 8192 at every row count fits -- and RMSN_ERR_HIP when the scratch cannot
+ * ever.  Returns RMSN_ERR_WORKSPACE when the workspace of the route it
+ * takes (rmsnorm_bwd_workspace_size_for_route of rmsnorm_bwd_route) exceeds
+ * the scratch -- every width up to 8192 at every row count fits -- and
+ * RMSN_ERR_HIP when the scratch cannot
  * be set up.  Every call on one GPU shares that GPU's scratch: calls that
  * may overlap in time on one GPU (different streams, host threads) race and
  * must be serialised by the caller.

@@ -174,12 +174,14 @@ __device__ __forceinline__ void bwd_rows(const BwdParams& p, int chunk, int nchu
 
     // With PF the workgroup loads its next rows while the current ones are
     // reduced (a second register tile), the first rows before the weights
-    // are widened.  Gated rows of one vector per lane always do: their
-    // workgroups fill a compute unit alone, so no other wavefront covers the
-    // load latency, and the tile fits the registers that occupancy leaves.
-    // Plain rows do when the route asks (PFP): where each compute unit holds
-    // few workgroups, as at a few thousand rows.  Results do not depend on it.
-    constexpr bool PF = GATE ? V == 1 : PFP;
+    // are widened.  Gated rows always do, up to H 8192: their arithmetic per
+    // element is long and one or two workgroups fill a compute unit, so no
+    // other wavefront covers the load latency (gated T 65536, H 4096: 509 ->
+    // 467 us with the tile, although its two-vector rows drop to one
+    // wavefront per SIMD; wider gated rows would spill).  Plain rows do when
+    // the route asks (PFP): where each compute unit holds few workgroups, as
+    // at a few thousand rows.  Results do not depend on it.
+    constexpr bool PF = GATE ? LPR * V * 8 <= 8192 : PFP;
     constexpr bool DEFER = PF && !DRES;  // see BwdTile
     using Tile = BwdTile<U, V, DRES, GATE, DEFER>;
     Tile cur;

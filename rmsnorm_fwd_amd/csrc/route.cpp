@@ -80,18 +80,22 @@ static int64_t cols_max_elems(int64_t H)
 // The next-row tile of the row kernel (BwdRoute::prefetch), by width: the
 // largest row count that takes it on plain rows, the row count from which
 // it takes 512 workgroups instead of 256, and the same two for rows with
-// dres.  Measured on MI355X with cold caches (BF16 w, FP32 w at H 4096;
-// T 1024-131072): on plain rows the tile wins 2-11 % up to a few thousand
-// rows, where each compute unit holds one or two workgroups and no other
-// wavefront covers the load latency (T 4096, H 1536: 19.0 -> 17.8 us;
-// T 2048, H 5120: 28.1 -> 25.8 us; T 2048, H 4096: 24.0 -> 21.3 us), and
-// loses 1-10 % beyond, where it only adds registers (T 65536, H 4096:
-// 264 -> 283 us); it never wins at H 8192 and spills at H 16384.  With
-// dres, three loads per element, it wins at every row count measured from
-// H 1024 to 6144 (T 131072, H 6144: 1176 -> 1048 us; T 65536, H 4096:
-// 373 -> 351 us).  At H <= 128 it moved nothing beyond 1-3 %.  With dres a
-// route never takes more workgroups than without at the same row count, so
-// a workspace sized for plain rows also serves rows with dres.
+// dres.  Measured on MI355X with cold caches (BF16 w; T 2048-131072,
+// chunk counts 128-512 with and without the tile): on plain rows the tile
+// wins 7-16 % at a few thousand rows, where each compute unit holds one or
+// two workgroups and no other wavefront covers the load latency (T 4096,
+// H 1536: 18.6 -> 16.6 us; T 2048, H 5120: 28.0 -> 23.5 us; T 4096,
+// H 4096: 32.6 -> 28.3 us), 3-5 % up to 16384 rows, and at H 1024, 1536
+// and 8192 at every row count measured (T 65536, H 8192: 586 -> 559 us);
+// elsewhere beyond 16384-65536 rows it only adds registers and loses 1-6 %
+// (T 65536, H 4096: 268 -> 272 us; T 65536, H 2048: 139 -> 146 us).  256
+// workgroups (two or more iterations each, which the tile overlaps) beat
+// 384 and 512 except at H 1024 from 16384 rows.  With dres, three loads
+// per element, the tile (without the deferred rstd, see bwd.hip) wins at
+// every row count measured from H 1024 to 6144 (T 131072, H 6144: 1176 ->
+// 1048 us; T 65536, H 4096: 373 -> 351 us).  It spills at H 16384.  With
+// dres a route never takes more workgroups than without at the same row
+// count, so a workspace sized for plain rows also serves rows with dres.
 struct TileWindow {
     int64_t max_h;       // serves H <= max_h (the smallest such entry)
     int64_t rows;        // plain rows: the tile up to this many rows
@@ -101,14 +105,17 @@ struct TileWindow {
 };
 constexpr int64_t kAllRows = int64_t(1) << 40;
 static constexpr TileWindow kTileWindows[] = {
-    {128, 0, 0, 0, 0},
-    {512, 16384, kAllRows, 16384, kAllRows},
-    {1024, 8192, 6144, kAllRows, 6144},
-    {2048, 8192, kAllRows, kAllRows, kAllRows},
-    {3072, 8192, 6144, kAllRows, kAllRows},
-    {4096, 8192, kAllRows, kAllRows, kAllRows},
-    {5120, 16384, 4096, kAllRows, kAllRows},  // T 8192: 57.8 -> 56.0 us; T 16384: 96.4 -> 93.9 us
-    {6144, 4096, kAllRows, kAllRows, kAllRows},  // T 8192 even
+    {128, 0, 0, 0, 0},                                // not measured beyond 1-3 %
+    {256, 65536, kAllRows, 65536, kAllRows},          // T 32768: 19.2 -> 18.4 us
+    {512, 32768, kAllRows, 32768, kAllRows},          // T 65536: 2.8 % slower
+    {1024, kAllRows, 16384, kAllRows, 16384},         // T 65536: 78.2 -> 75.5 us
+    {1536, kAllRows, kAllRows, kAllRows, kAllRows},   // T 65536: 108.7 -> 104.8 us
+    {2048, 16384, kAllRows, kAllRows, kAllRows},      // T 65536: 5 % slower
+    {3072, 32768, kAllRows, kAllRows, kAllRows},      // T 65536: 1.3 % slower
+    {4096, 16384, kAllRows, kAllRows, kAllRows},      // T 32768: 0.9 % slower
+    {5120, 16384, kAllRows, kAllRows, kAllRows},      // T 32768 even
+    {6144, 16384, kAllRows, kAllRows, kAllRows},      // T 32768: 1.4 % slower
+    {8192, kAllRows, kAllRows, 0, 0},                 // dres: even
     {16384, 0, 0, 0, 0},
 };
 
@@ -150,17 +157,26 @@ BwdRoute pair_route(int64_t R, int64_t H, bool residual, bool gated)
     // size, measured twice (with the next-row tile: 18.1 -> 21.8 us at
     // T 4096, H 1536, 26.3 with 32-column reduce workgroups; 265 -> 269 us
     // at T 65536, H 4096).
-    // The gated backward keeps the chunking it was measured with: up to
-    // R * H = 12 M elements 384 workgroups, the layout's count above.  Its
-    // rows load ahead by their own rule (one vector per lane) or not at all,
-    // and the tile window's 256 workgroups were slower for them at H 1536 -
-    // 4096 (T 8192, H 1536: 46 -> 67 us; T 4096, H 4096: 46 -> 56 us),
-    // faster only at H 6144 (T 2048: 47 -> 42 us).
     const int64_t per = (4 + rpi - 1) / rpi;  // row groups per workgroup
     int64_t c = (groups + per - 1) / per;
     if (c < 128) c = groups < 128 ? groups : 128;
-    if (gated && R * H <= 12000000 && c > 384) c = 384;
-    if (c > L.k) c = L.k;
+    if (gated && H > 1024 && H <= 8192) {
+        // The gated rows (which always load their next rows ahead) fill a
+        // compute unit with one or two workgroups, so their counts are
+        // multiples of the 256 compute units (384 left units idle: T 4096,
+        // H 3072: 44.7 against 36.1 us at 256): 512 at H 1536 (T 4096:
+        // 27.4 -> 24.8 us at 512), 256 at H 5120 - 6144 up to 65536 rows
+        // (T 65536: 766 -> 726 us; T 131072: 512 by 1.9 %), 256 up to
+        // 16384 rows and 512 above at the other widths (T 16384, H 8192:
+        // 277 -> 235 us at 256; T 65536: 512 by 1.5 %).
+        const bool wide = H > 4096 && H <= 6144;
+        const int64_t g = H <= 1536 ? 512 : R <= (wide ? 65536 : 16384) ? 256 : 512;
+        c = g < groups ? g : groups;
+    } else {
+        // narrower and wider gated rows: as measured before the tile
+        if (gated && R * H <= 12000000 && c > 384) c = 384;
+        if (c > L.k) c = L.k;
+    }
     return BwdRoute{FORM_PAIR, (int)(c > 0 ? c : 1), 0, 0, 0};
 }
 
