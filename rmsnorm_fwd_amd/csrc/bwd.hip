@@ -182,7 +182,10 @@ __device__ __forceinline__ void bwd_rows(const BwdParams& p, int chunk, int nchu
     // the route asks (PFP): where each compute unit holds few workgroups, as
     // at a few thousand rows.  Results do not depend on it.
     constexpr bool PF = GATE ? LPR * V * 8 <= 8192 : PFP;
-    constexpr bool DEFER = PF && !DRES;  // see BwdTile
+    // see BwdTile: with the tile, no dres (the column forms' plain row
+    // tasks, one or a few iterations each beside the column tasks, measured
+    // 1-2 % slower deferred: T 449, H 6144: 12.15 -> 12.43 us)
+    constexpr bool DEFER = PF && !DRES;
     using Tile = BwdTile<U, V, DRES, GATE, DEFER>;
     Tile cur;
     BwdTile<PF ? U : 1, PF ? V : 1, DRES, GATE, DEFER> nxt;
@@ -337,7 +340,7 @@ __device__ __forceinline__ void bwd_rows(const BwdParams& p, int chunk, int nchu
             }
         }
     };
-    if constexpr (DEFER) {
+    if constexpr (PF && DEFER) {
         // The loop runs while a next iteration exists and loads it
         // unconditionally, the last iteration after it: every path into the
         // work then has the same loads in flight, so the wait before the
