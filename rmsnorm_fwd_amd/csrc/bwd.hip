@@ -89,9 +89,10 @@ __device__ __forceinline__ double chunk_group_sum(const double* part, int chunks
 //
 // rstd: with DEFER it is loaded unconditionally (rr is in range) and widened
 // and masked only where it is used, so nothing in the load waits and the
-// row's other loads go out behind it at once; without, it is masked and
-// widened as it arrives, and that wait also drains the wavefront's earlier
-// stores before the row's loads go out.  The second is faster for rows that
+// row's other loads go out behind it at once; without, all U rows' rstd are
+// loaded, waited for together and widened, and that wait also drains the
+// wavefront's earlier stores before the rows' loads go out (one wait instead
+// of one per row: 1-2 % at H 256-2048 and with dres).  The second is faster for rows that
 // stream at full occupancy (each wavefront's reads and writes stay in
 // separate phases: T 131072, H 6144: 738 against 865 us), the first where
 // few wavefronts share a compute unit and the next-row tile is in use
@@ -109,6 +110,11 @@ template <int U, int V, int SLOTS, bool DRES, bool GATE, bool DEFER>
 __device__ __forceinline__ void bwd_load(BwdTile<U, V, DRES, GATE, DEFER>& t, const BwdParams& p,
                                          const LaneVectors<V>& lv, int base, int slot, int row1)
 {
+    // The workgroup-wide rows of two per iteration (H 4096) keep one wait
+    // per row: 1 % faster there than one wait (T 65536: 266.4 against 267.8
+    // us), where the other layouts gain 1-2 % from it.
+    constexpr bool PER_ROW = !DEFER && U > 1 && SLOTS == 1;
+    float rf[U];
 #pragma unroll
     for (int u = 0; u < U; ++u) {
         const int row = base + u * SLOTS + slot;
@@ -116,7 +122,15 @@ __device__ __forceinline__ void bwd_load(BwdTile<U, V, DRES, GATE, DEFER>& t, co
         const int rr = t.ok[u] ? row : row1 - 1;  // rows past the end re-read the last row
         t.off[u] = row_offset(rr, p.rows);
         if constexpr (DEFER) t.rho[u] = p.rstd[rr];
-        else t.rho[u] = t.ok[u] ? (double)p.rstd[rr] : 0.0;  // ... and add nothing to dw
+        else if constexpr (PER_ROW) t.rho[u] = t.ok[u] ? (double)p.rstd[rr] : 0.0;  // ... and add nothing to dw
+        else rf[u] = p.rstd[rr];
+    }
+    if constexpr (!DEFER && !PER_ROW) {
+        // one wait for all U rows' rstd (not one per row), which also drains
+        // the wavefront's earlier stores before the rows' loads go out
+        __builtin_amdgcn_s_waitcnt(0);
+#pragma unroll
+        for (int u = 0; u < U; ++u) t.rho[u] = t.ok[u] ? (double)rf[u] : 0.0;  // ... rows past the end add nothing
     }
 #pragma unroll
     for (int u = 0; u < U; ++u)
