@@ -106,14 +106,10 @@ struct BwdTile {
     uint4 rv[(DRES || GATE) ? U : 1][(DRES || GATE) ? V : 1];
 };
 
-template <int U, int V, int SLOTS, bool DRES, bool GATE, bool DEFER>
+template <int U, int V, int SLOTS, bool DRES, bool GATE, bool DEFER, bool PER_ROW>
 __device__ __forceinline__ void bwd_load(BwdTile<U, V, DRES, GATE, DEFER>& t, const BwdParams& p,
                                          const LaneVectors<V>& lv, int base, int slot, int row1)
 {
-    // The workgroup-wide rows of two per iteration (H 4096) keep one wait
-    // per row: 1 % faster there than one wait (T 65536: 266.4 against 267.8
-    // us), where the other layouts gain 1-2 % from it.
-    constexpr bool PER_ROW = !DEFER && U > 1 && SLOTS == 1;
     float rf[U];
 #pragma unroll
     for (int u = 0; u < U; ++u) {
@@ -200,11 +196,17 @@ __device__ __forceinline__ void bwd_rows(const BwdParams& p, int chunk, int nchu
     // tasks, one or a few iterations each beside the column tasks, measured
     // 1-2 % slower deferred: T 449, H 6144: 12.15 -> 12.43 us)
     constexpr bool DEFER = PF && !DRES;
+    // Without DEFER the row kernel waits once for an iteration's rstd
+    // values; the workgroup-wide rows of two per iteration (H 4096) and the
+    // column forms' row tasks keep one wait per row (1 % faster there: T
+    // 65536, H 4096: 266.4 against 267.8 us; T 449, H 6144: 12.3 against
+    // 12.5 us), where the other row kernels gain 1-2 % from one wait.
+    constexpr bool PER_ROW = !DEFER && ((U > 1 && SLOTS == 1) || !DW);
     using Tile = BwdTile<U, V, DRES, GATE, DEFER>;
     Tile cur;
     BwdTile<PF ? U : 1, PF ? V : 1, DRES, GATE, DEFER> nxt;
     if constexpr (PF) {
-        if (first < row1) bwd_load<U, V, SLOTS, DRES, GATE, DEFER>(cur, p, lv, first, slot, row1);
+        if (first < row1) bwd_load<U, V, SLOTS, DRES, GATE, DEFER, PER_ROW>(cur, p, lv, first, slot, row1);
     }
     // The weights in FP64 registers, 0 for vectors a lane does not own; rows
     // wider than 8192 (four or more vectors per lane) keep them as loaded
@@ -364,7 +366,7 @@ __device__ __forceinline__ void bwd_rows(const BwdParams& p, int chunk, int nchu
             int it = 0;
             int base = first;
             for (; base + step < row1; base += step, ++it) {
-                bwd_load<U, V, SLOTS, DRES, GATE, DEFER>(nxt, p, lv, base + step, slot, row1);
+                bwd_load<U, V, SLOTS, DRES, GATE, DEFER, PER_ROW>(nxt, p, lv, base + step, slot, row1);
                 work(cur, it);
                 cur = nxt;
             }
@@ -374,9 +376,9 @@ __device__ __forceinline__ void bwd_rows(const BwdParams& p, int chunk, int nchu
         int it = 0;
         for (int base = first; base < row1; base += step, ++it) {
             if constexpr (PF) {
-                if (base + step < row1) bwd_load<U, V, SLOTS, DRES, GATE, DEFER>(nxt, p, lv, base + step, slot, row1);
+                if (base + step < row1) bwd_load<U, V, SLOTS, DRES, GATE, DEFER, PER_ROW>(nxt, p, lv, base + step, slot, row1);
             } else {
-                bwd_load<U, V, SLOTS, DRES, GATE, DEFER>(cur, p, lv, base, slot, row1);
+                bwd_load<U, V, SLOTS, DRES, GATE, DEFER, PER_ROW>(cur, p, lv, base, slot, row1);
             }
             work(cur, it);
             if constexpr (PF) {
