@@ -127,7 +127,7 @@ def run_gated(L: Layout, wdt="bf16", seed=0, kind="mixed", det_repeats=2):
     return ulp_dist(first["dx"], ref_dx).max(initial=0), ulp_dist(first["dg"], ref_dg).max(initial=0)
 
 
-@pytest.mark.parametrize("H", [8, 64, 256, 264, 1024, 1536, 2048, 4096, 5120, 6144, 8192])
+@pytest.mark.parametrize("H", [8, 64, 256, 264, 1024, 1536, 2048, 4096, 5120, 6144, 8192, 8200, 16384])
 @pytest.mark.parametrize("wdt", ["bf16", "f32"])
 def test_gated_widths(H, wdt):
     T = 37 if H >= 4096 else 301
@@ -177,12 +177,18 @@ def test_gated_head_view():
     print(run_gated(Layout.heads_view(512, 24, 256, 8192, 256), "bf16", seed=3))
 
 
-@pytest.mark.parametrize("T,H", [(4099, 1536), (4099, 3072), (4099, 5120), (4099, 6144), (40000, 64)])
-def test_gated_rows_over_several_iterations(T, H):
-    # one-vector gated rows load a workgroup's next rows while reducing the
-    # current ones; these row counts give every workgroup several iterations
-    # and a ragged last one
-    print(T, H, run_gated(Layout.plain(T, H), "bf16", seed=T + H))
+@pytest.mark.parametrize("T,H,wdt", [(4099, 1536, "bf16"), (4099, 3072, "bf16"), (4099, 5120, "bf16"),
+                                     (4099, 6144, "bf16"), (60000, 64, "bf16"), (4099, 2048, "f32"),
+                                     (4099, 4096, "bf16"), (1500, 8192, "f32"), (1500, 8200, "bf16"),
+                                     (1100, 16384, "bf16")])
+def test_gated_rows_over_several_iterations(T, H, wdt):
+    # gated rows up to H 8192 load a workgroup's next rows while reducing the
+    # current ones (one- and two-vector rows, and the H 8192 rows run as 512
+    # lanes x 2 vectors), wider ones do not; these row counts take the row
+    # kernel with several iterations per workgroup and a ragged last one
+    import rmsnorm_fwd_amd as rn
+    assert rn.rmsnorm_gated_bwd_route(T, 1, H, 0, 1)[0] == rn.RMSN_FORM_PAIR
+    print(T, H, wdt, run_gated(Layout.plain(T, H), wdt, seed=T + H))
 
 
 def test_gated_large():

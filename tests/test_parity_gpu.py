@@ -30,7 +30,7 @@ def test_widths(H, wdt):
     print(H, wdt, rep)
 
 
-@pytest.mark.parametrize("H", [256, 1536, 4096, 5120, 6144])
+@pytest.mark.parametrize("H", [256, 1536, 4096, 5120, 6144, 8192, 8200, 16384])
 @pytest.mark.parametrize("wdt", ["bf16", "f32"])
 @pytest.mark.parametrize("dres", [False, True])
 def test_residual(H, wdt, dres):
