@@ -17,7 +17,17 @@
 // rounded to FP32, then BF16 (within one BF16 unit of the exact value).  The
 // row dot's order depends only on H, so dx is the same in both modes and for
 // every chunking.  The weights live in registers as FP64 (0 for vectors a
-// lane does not own).
+// lane does not own); rows wider than 8192 keep them as loaded and widen
+// each where it is used.
+//
+// Loads.  A workgroup loads an iteration's rows (x or h, dy, rstd, and dres
+// or the gate) before it uses any of them.  With the next-row tile (a route
+// choice for plain rows, always for gated rows up to H 8192) it loads the
+// next iteration's rows while it works on the current ones; the order of
+// its waits on the memory counter, which also counts stores, is chosen per
+// kernel (BwdTile): the tile needs them to leave the next rows' loads in
+// flight, full-occupancy rows are faster when each wait drains the
+// wavefront's earlier stores first.  None of this changes a result bit.
 //
 // dw.  Each lane keeps FP64 column sums over the chunk's rows in registers;
 // row groups of one workgroup are added by lane exchanges inside a
@@ -87,16 +97,21 @@ __device__ __forceinline__ double chunk_group_sum(const double* part, int chunks
 // dres, or the gate g) vectors, all loaded before any of them is used.
 // DRES and GATE never meet.
 //
-// rstd: with DEFER it is loaded unconditionally (rr is in range) and widened
-// and masked only where it is used, so nothing in the load waits and the
-// row's other loads go out behind it at once; without, all U rows' rstd are
-// loaded, waited for together and widened, and that wait also drains the
-// wavefront's earlier stores before the rows' loads go out (one wait instead
-// of one per row: 1-2 % at H 256-2048 and with dres).  The second is faster for rows that
-// stream at full occupancy (each wavefront's reads and writes stay in
-// separate phases: T 131072, H 6144: 738 against 865 us), the first where
-// few wavefronts share a compute unit and the next-row tile is in use
-// (T 4096, H 1536: 18.0 -> 16.8 us; gated T 16384, H 3072: 169 -> 110 us).
+// rstd, three ways (one memory counter covers loads and stores, and a wait
+// on it drains everything issued before):
+//   DEFER    loaded unconditionally (rr is in range) and widened and masked
+//            only where it is used, so nothing in the load waits and the
+//            rows' other loads go out behind it at once;
+//   PER_ROW  masked and widened as each row's value arrives, a wait per row,
+//            each of which also drains the wavefront's earlier stores;
+//   else     all U rows' values loaded, one wait, then widened and masked.
+// The waits that drain the stores before a row's loads go out are faster
+// where rows stream at full occupancy (each wavefront's reads and writes
+// stay in separate phases: T 131072, H 6144: 738 against 865 us deferred),
+// one wait for all rows is 1-2 % faster than one per row at most widths,
+// and DEFER is faster where few wavefronts share a compute unit and the
+// next-row tile is in use (T 4096, H 1536: 18.0 -> 16.8 us; gated T 16384,
+// H 3072: 169 -> 110 us).
 template <int U, int V, bool DRES, bool GATE, bool DEFER>
 struct BwdTile {
     bool ok[U];
