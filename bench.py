@@ -647,13 +647,25 @@ PROFILE_SOURCES = {"fwd_kernel": ["fwd.hip", "device_common.h", "kernels.h", "la
                    "dw_reduce_kernel": ["bwd.hip", "device_common.h", "kernels.h", "layouts.h"]}
 
 
+def code_text(src):
+    """C/C++ source without its comments, whitespace collapsed: what a
+    profile's figures depend on (string and character literals are kept)."""
+    import re
+
+    tok = re.compile(r'("(?:\\.|[^"\\\n])*"|\'(?:\\.|[^\'\\\n])*\')|//[^\n]*|/\*.*?\*/', re.S)
+    body = tok.sub(lambda m: m.group(1) if m.group(1) else " ", src)
+    return re.sub(r"\s+", " ", body).strip()
+
+
 def source_hash(kernel):
+    """Hash of the code (not the comments) of the sources a kernel is built
+    from; a profile summary whose hash no longer matches is stale."""
     import hashlib
 
     h = hashlib.sha256()
     for f in PROFILE_SOURCES[kernel]:
-        with open(os.path.join(ROOT, "rmsnorm_fwd_amd", "csrc", f), "rb") as fh:
-            h.update(fh.read())
+        with open(os.path.join(ROOT, "rmsnorm_fwd_amd", "csrc", f), encoding="utf-8") as fh:
+            h.update(code_text(fh.read()).encode())
     return h.hexdigest()[:16]
 
 
@@ -775,7 +787,7 @@ def profile_report(out_dir, workload, steps, warmup):
         out.append(f"| `{name[:90]}` | {fb:,.1f} | {wb:,.1f} | {total:,} | {source_hash(k)} |")
         if k not in rec["kernels"]:
             rec["kernels"][k] = {"traffic_bytes": total, "source_hash": source_hash(k), "kernel": name}
-    out += ["", "Machine-readable (read by bench.py; a source hash that no longer matches the sources means the "
+    out += ["", "Machine-readable (read by bench.py; a source hash (of the code, comments excluded) that no longer matches the sources means the "
             "figure is stale):", "", "```json", json.dumps(rec, indent=1), "```", ""]
     return "\n".join(out)
 

@@ -105,3 +105,19 @@ def test_profile_report_scales_counters_and_averages_the_last_run(tmp_path):
     nb = b.fwd_bytes(131072, 6144, 2, True)
     assert f"| fwd | {nb:,} |" in md and f"1200.00 ({nb / 1200e-6 / 8e12:.4f})" in md
     assert "python3 R/bench.py --profile-report OUT T131072_H6144_res 2 1" in md
+
+
+def test_profile_hash_follows_code_not_comments():
+    # a profile summary stays valid across comment and layout edits of the
+    # sources, and goes stale on any change to the code itself (string and
+    # character literals that hold comment markers are code)
+    import bench
+    a = 'int f(int x) { // sum\n  return x + 1; /* one */ }\nconst char* s = "a // b";\n'
+    b = '/* header */\nint f(int x) {\n    return x + 1;   // one\n}\nconst char* s = "a // b";'
+    c = 'int f(int x) { return x + 2; }\nconst char* s = "a // b";'
+    d = 'int f(int x) { return x + 1; }\nconst char* s = "a // c";'
+    assert bench.code_text(a) == bench.code_text(b)
+    assert bench.code_text(a) != bench.code_text(c)
+    assert bench.code_text(a) != bench.code_text(d)
+    assert bench.code_text("char q = '\\''; // x") == "char q = '\\'';"
+    assert len(bench.source_hash("bwd_kernel")) == 16
