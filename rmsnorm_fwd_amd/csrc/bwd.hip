@@ -281,6 +281,14 @@ __device__ __forceinline__ void bwd_rows(const BwdParams& p, int chunk, int nchu
         uint4 (&xv)[U][V] = t.xv;
         uint4 (&dv)[U][V] = t.dv;
         double S[U];
+        // Gated rows take sigmoid(g) eight values at a time (sigmoid8) in
+        // the first pass and keep it for the second, except where that was
+        // measured slower on MI355X: rows wider than 4096 have no registers
+        // for it (it spills), and the two-vector layouts of 128 and 256
+        // lanes (H 2048, 4096) lose at 65536 rows.  Those evaluate sigmoid
+        // per element in both passes; both forms give the same bits.
+        constexpr bool KEEP_SG = GATE && LPR * V * 8 <= 4096 && !(LPR >= 128 && V == 2);
+        float sgk[KEEP_SG ? U : 1][KEEP_SG ? V : 1][8];
 #pragma unroll
         for (int u = 0; u < U; ++u) {
             S[u] = 0.0;
@@ -293,8 +301,14 @@ __device__ __forceinline__ void bwd_rows(const BwdParams& p, int chunk, int nchu
                 if constexpr (GATE) {
                     float gf[8];
                     unpack8(t.rv[u][v], gf);
+                    if constexpr (KEEP_SG) {
+                        sigmoid8(gf, sgk[u][v]);
 #pragma unroll
-                    for (int e = 0; e < 8; ++e) sg[e] = gf[e] * sigmoid_f32(gf[e]);
+                        for (int e = 0; e < 8; ++e) sg[e] = gf[e] * sgk[u][v][e];
+                    } else {
+#pragma unroll
+                        for (int e = 0; e < 8; ++e) sg[e] = gf[e] * sigmoid_f32(gf[e]);
+                    }
                 }
 #pragma unroll
                 for (int e = 0; e < 8; ++e) {
@@ -346,7 +360,7 @@ __device__ __forceinline__ void bwd_rows(const BwdParams& p, int chunk, int nchu
 #pragma unroll
                     for (int e = 0; e < 8; ++e) {
                         const float wf = wf32(v, e);
-                        const float sgm = sigmoid_f32(rf[e]);
+                        const float sgm = KEEP_SG ? sgk[u][v][e] : sigmoid_f32(rf[e]);
                         const float dsilu = sgm * __builtin_fmaf(rf[e], 1.0f - sgm, 1.0f);
                         const float ef = df[e] * (rf[e] * sgm);
                         q[e] = (df[e] * ((xf[e] * rf32) * wf)) * dsilu;

@@ -137,11 +137,20 @@ __global__ void __launch_bounds__(block_of(LPR)) fwd_kernel(FwdParams p)
 #pragma unroll
                 for (int e = 0; e < 8; ++e) f[e] = (f[e] * rs) * wv[e];
                 if constexpr (GATE) {
-                    // y = (u * rstd * w) * silu(g), all in FP32
-                    float gf[8];
+                    // y = (u * rstd * w) * silu(g), all in FP32.  sigmoid8
+                    // (same bits as sigmoid_f32) is slower where a row spans
+                    // several wavefronts and a lane holds more than one row
+                    // (measured on MI355X: H 2048, 4096, 8192).
+                    float gf[8], sgv[8];
                     unpack8(cur.rv[u][v], gf);
+                    if constexpr (LPR >= 256 && U > 1) {
 #pragma unroll
-                    for (int e = 0; e < 8; ++e) f[e] *= gf[e] * sigmoid_f32(gf[e]);
+                        for (int e = 0; e < 8; ++e) sgv[e] = sigmoid_f32(gf[e]);
+                    } else {
+                        sigmoid8(gf, sgv);
+                    }
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) f[e] *= gf[e] * sgv[e];
                 }
                 if (ok[u] && lv.ok[v]) st16_stream(p.y + off[u] + lv.col[v], pack8(f));
             }
