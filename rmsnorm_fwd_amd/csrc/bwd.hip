@@ -282,12 +282,12 @@ __device__ __forceinline__ void bwd_rows(const BwdParams& p, int chunk, int nchu
         uint4 (&dv)[U][V] = t.dv;
         double S[U];
         // Gated rows take sigmoid(g) eight values at a time (sigmoid8) in
-        // the first pass and keep it for the second, except where that was
-        // measured slower on MI355X: rows wider than 4096 have no registers
-        // for it (it spills), and the two-vector layouts of 128 and 256
-        // lanes (H 2048, 4096) lose at 65536 rows.  Those evaluate sigmoid
-        // per element in both passes; both forms give the same bits.
-        constexpr bool KEEP_SG = GATE && LPR * V * 8 <= 4096 && !(LPR >= 128 && V == 2);
+        // the first pass and keep it for the second, up to H 4096 and in
+        // the one-vector rows of 768 lanes (H 5120, 6144).  The two-vector
+        // rows of 512 lanes and more (H 8192, 16384) have no registers for
+        // it (they spill) and evaluate sigmoid per element in both passes;
+        // both forms give the same bits.
+        constexpr bool KEEP_SG = GATE && (LPR * V * 8 <= 4096 || LPR == 768);
         float sgk[KEEP_SG ? U : 1][KEEP_SG ? V : 1][8];
 #pragma unroll
         for (int u = 0; u < U; ++u) {

@@ -140,10 +140,11 @@ __global__ void __launch_bounds__(block_of(LPR)) fwd_kernel(FwdParams p)
                     // y = (u * rstd * w) * silu(g), all in FP32.  sigmoid8
                     // (same bits as sigmoid_f32) is slower where a row spans
                     // several wavefronts and a lane holds more than one row
-                    // (measured on MI355X: H 2048, 4096, 8192).
+                    // (measured on MI355X: H 2048, 4096, 8192) and not
+                    // reliably faster on the 512-lane rows (H 16384).
                     float gf[8], sgv[8];
                     unpack8(cur.rv[u][v], gf);
-                    if constexpr (LPR >= 256 && U > 1) {
+                    if constexpr (LPR >= 512 || (LPR >= 256 && U > 1)) {
 #pragma unroll
                         for (int e = 0; e < 8; ++e) sgv[e] = sigmoid_f32(gf[e]);
                     } else {

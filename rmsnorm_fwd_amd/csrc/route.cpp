@@ -165,12 +165,13 @@ BwdRoute pair_route(int64_t R, int64_t H, bool residual, bool gated)
         // compute unit with one or two workgroups, so their counts are
         // multiples of the 256 compute units (384 left units idle: T 4096,
         // H 3072: 44.7 against 36.1 us at 256): 512 at H 1536 (T 4096:
-        // 27.4 -> 24.8 us at 512), 256 at H 5120 - 6144 up to 65536 rows
-        // (T 65536: 766 -> 726 us; T 131072: 512 by 1.9 %), 256 up to
-        // 16384 rows and 512 above at the other widths (T 16384, H 8192:
-        // 277 -> 235 us at 256; T 65536: 512 by 1.5 %).
-        const bool wide = H > 4096 && H <= 6144;
-        const int64_t g = H <= 1536 ? 512 : R <= (wide ? 65536 : 16384) ? 256 : 512;
+        // 27.4 -> 24.8 us at 512; T 131072: 409 against 522 us at 256),
+        // 256 at every row count from H 1537 to 6144 (T 131072, H 6144:
+        // 1472 against 1549 us at 512; H 4096, whose rows then run at two
+        // wavefronts per SIMD: 921 against 1206 us), and 256 up to 65536
+        // rows and 512 above for the wider rows (T 16384, H 8192: 277 ->
+        // 235 us at 256; T 131072: 512 by 1.8 %).
+        const int64_t g = H <= 1536 ? 512 : (H <= 6144 || R <= 65536) ? 256 : 512;
         c = g < groups ? g : groups;
     } else {
         // narrower and wider gated rows: as measured before the tile
