@@ -321,7 +321,7 @@ __device__ __forceinline__ void bwd_rows(const BwdParams& p, int chunk, int nchu
                 }
             }
         }
-        row_group_sum<LPR, U, RPI>(S, red, it, slot, g);
+        row_group_sum<LPR, U, RPI, true>(S, red, it, slot, g);
         if constexpr (WRAW || (GATE && LPR >= 1024)) {
             // Wide rows: unpack the tile again in the second pass rather
             // than hold the first pass's FP32 values across the row

@@ -208,8 +208,12 @@ __device__ __forceinline__ float rstd_from_ms(double m)
 // Reduce U per-row values across the LPR lanes of each row group.  For
 // LPR > 64 the wavefronts of a row meet in LDS (double-buffered by iteration
 // parity, one barrier per iteration); the wavefront partials are added in
-// wavefront order.
-template <int LPR, int U, int RPI>
+// wavefront order.  With ONE_ROW_AT_A_TIME the partials of one row are read
+// and added before the next row's are read (an empty asm with a memory
+// clobber keeps the compiler from hoisting the reads), so at most one row's
+// partials occupy registers; otherwise all of them may be in flight at once.
+// The sums are the same either way.
+template <int LPR, int U, int RPI, bool ONE_ROW_AT_A_TIME = false>
 __device__ __forceinline__ void row_group_sum(double (&s)[U], double (*red)[RPI][LPR > 64 ? LPR / 64 : 1],
                                               int it, int slot, int g)
 {
@@ -229,6 +233,7 @@ __device__ __forceinline__ void row_group_sum(double (&s)[U], double (*red)[RPI]
             double t = red[it & 1][u * SLOTS + slot][0];
 #pragma unroll
             for (int k = 1; k < W; ++k) t += red[it & 1][u * SLOTS + slot][k];
+            if constexpr (ONE_ROW_AT_A_TIME) __asm__ volatile("" : "+v"(t)::"memory");
             s[u] = t;
         }
     }
