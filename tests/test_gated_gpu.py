@@ -144,6 +144,14 @@ def test_gated_gate_families(kind):
     print(kind, run_gated(Layout.plain(2048, 2048), "bf16", seed=7, kind=kind))
 
 
+@pytest.mark.parametrize("H", [64, 512, 1536, 3072, 4096, 5120, 6144, 16384])
+def test_gated_moderate_gates_widths(H):
+    # N(0,1) gates: no gate reaches the scaled branch of the sigmoid (g below
+    # about -44), so every lane of the eight-gate form takes its direct path
+    T = 37 if H >= 4096 else 301
+    print(H, run_gated(Layout.plain(T, H), "bf16", seed=H + 11, kind="normal"))
+
+
 @pytest.mark.parametrize("H", [64, 2048, 6144])
 def test_gated_infinite_gates_forward(H):
     # g = -inf gives silu = -inf * 0 = NaN and g = +inf gives +inf, as the
