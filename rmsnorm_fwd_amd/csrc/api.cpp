@@ -95,6 +95,7 @@ int bwd_impl(const void* dy, const void* x, const float* rstd, const void* w, in
     p.form = r.form;
     p.direct_dw = r.form == FORM_PAIR && r.chunks == 1;
     p.prefetch = r.prefetch;
+    p.one_row = s.heads > 1 && (s.sh != s.H || s.st != s.heads * s.H);
     p.inv_h = 1.0 / (double)s.H;
     const bool w32 = w_dtype == RMSN_W_F32;
     if (r.form == FORM_COLS || r.form == FORM_COLS_TICKET) {

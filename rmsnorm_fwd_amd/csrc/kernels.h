@@ -69,6 +69,7 @@ struct BwdParams {
     int slices;           // column forms: column slices, ceil(H / (8 col_vecs))
     int col_tasks;        // column forms: column tasks at the start of this launch's grid (0: row tasks only)
     int prefetch;         // row kernel over several chunks, plain rows: 1 = next-row register tile
+    int one_row;          // per-head view with gaps between rows: one row per row group (H 129-256)
     double inv_h;
 };
 

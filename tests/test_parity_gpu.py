@@ -132,6 +132,23 @@ def test_head_views(layout, wdt):
     print(layout, wdt, rep)
 
 
+@pytest.mark.parametrize("T,heads,H,st,sh,res", [
+    (1024, 24, 256, 8192, 256, False),    # pair with the next-row tile, one row per row group
+    (1024, 24, 200, 8192, 256, True),     # the same at H 200, residual and dres
+    (3000, 24, 256, 8192, 256, False),    # above the tile's window (72000 rows)
+    (3000, 8, 256, 4096, 512, True),      # gaps between heads too
+    (20000, 4, 256, 1024, 256, False),    # contiguous: two rows per row group
+])
+@pytest.mark.parametrize("wdt", ["bf16", "f32"])
+def test_gapped_head_views_row_kernel(T, heads, H, st, sh, res, wdt):
+    # views with gaps between rows take one row per row group in the row
+    # kernel at H 129-256; these sizes route to the pair
+    import rmsnorm_fwd_amd as rn
+    assert rn.rmsnorm_bwd_route(T, heads, H, 0, res, 1)[0] == rn.RMSN_FORM_PAIR
+    rep = run_case(Layout.heads_view(T, heads, H, st, sh), wdt, res=res, dres=res, seed=T + H)
+    print(T, heads, H, st, sh, res, wdt, rep)
+
+
 @pytest.mark.parametrize("family", ["normal", "outlier", "offset"])
 def test_input_families(family):
     rep = run_case(Layout.plain(2048, 4096), "f32", family=family, seed=5)
