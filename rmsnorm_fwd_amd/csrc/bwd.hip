@@ -361,8 +361,10 @@ __device__ __forceinline__ void bwd_rows(const BwdParams& p, int chunk, int nchu
                     for (int e = 0; e < 8; ++e) {
                         const float wf = wf32(v, e);
                         const float sgm = KEEP_SG ? sgk[u][v][e] : sigmoid_f32(rf[e]);
-                        const float dsilu = sgm * __builtin_fmaf(rf[e], 1.0f - sgm, 1.0f);
-                        const float ef = df[e] * (rf[e] * sgm);
+                        // silu' = sigmoid * (1 + g (1 - sigmoid)) = sigmoid + silu (1 - sigmoid)
+                        const float sl = rf[e] * sgm;  // silu(g), as in the first pass
+                        const float dsilu = __builtin_fmaf(sl, 1.0f - sgm, sgm);
+                        const float ef = df[e] * sl;
                         q[e] = (df[e] * ((xf[e] * rf32) * wf)) * dsilu;
                         d[e] = __builtin_fmaf(wf * ef, rf32, -(xf[e] * lf));
                     }
