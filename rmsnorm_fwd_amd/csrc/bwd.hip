@@ -694,9 +694,9 @@ static hipError_t bwd_w(bool w_f32, const BwdParams& p, hipStream_t s)
     return w_f32 ? bwd_t<LPR, V, U, true, DRES, GATE, PFP>(p, s) : bwd_t<LPR, V, U, false, DRES, GATE, PFP>(p, s);
 }
 
-// Gated rows hold one more input per element and evaluate silu twice: with
-// more than one row per row group they outgrow the 256 registers a lane has
-// at two wavefronts per SIMD, so they take one.
+// Gated rows hold one more input per element and sigmoid(g) between the two
+// passes: with more than one row per row group they outgrow the 256
+// registers a lane has at two wavefronts per SIMD, so they take one.
 template <int LPR, int V, int U>
 constexpr int gated_u() { return LPR <= 256 ? 1 : U; }
 
