@@ -282,6 +282,24 @@ def test_route_table_moves_from_column_forms_to_the_pair():
         assert prev == 2 and rn.rmsnorm_bwd_route(65536, 1, H, 0, 0, 1)[1] >= 256
 
 
+def test_gated_route_table():
+    # the gated backward's chunking (measured, see route.cpp): where it takes
+    # the pair, 512 workgroups at H 1025-1536, 256 at every row count from
+    # H 1537 to 6144, 256 up to 65536 rows and 512 above at H 6145-8192;
+    # never more workgroups than row groups; the next-row tile is not a
+    # route field there; both modes and weight dtypes alike
+    for H in (1032, 1536, 1544, 2048, 3072, 4096, 4104, 5120, 6144, 6152, 8192):
+        for T in (16384, 16385, 32768, 65536, 65537, 131072):
+            r = rn.rmsnorm_gated_bwd_route(T, 1, H, 0, 1)
+            assert r == rn.rmsnorm_gated_bwd_route(T, 1, H, 1, 0)
+            form, chunks, cc, cv, pf = r
+            assert form == rn.RMSN_FORM_PAIR and cc == cv == pf == 0
+            want = 512 if H <= 1536 else (256 if H <= 6144 or T <= 65536 else 512)
+            assert chunks == want, (H, T, r)
+            # the size query without dres covers the gated route
+            assert rn.rmsnorm_bwd_workspace_size(T, 1, H, 0, False) >= rn.rmsnorm_bwd_workspace_size_for_route(T, 1, H, r)
+
+
 def test_row_count_limit_is_below_2_pow_30():
     r = rn.RmsnRoute()
     L = rn.lib()
