@@ -181,6 +181,16 @@ def test_gated_infinite_gates_forward(H):
     assert (np.abs(rstd.cpu().numpy().astype(np.float64) - ref_rstd) / ref_rstd).max() <= 1e-6
 
 
+@pytest.mark.parametrize("T,H", [(4099, 2048), (4099, 3072), (4099, 4096), (70000, 1536), (4099, 6144)])
+def test_gated_rows_over_several_iterations_moderate_gates(T, H):
+    # N(0,1) gates (no lane takes the sigmoid's scaled branch) through the
+    # row kernel with several iterations per workgroup, on the layouts that
+    # keep sigmoid(g) between the two passes
+    import rmsnorm_fwd_amd as rn
+    assert rn.rmsnorm_gated_bwd_route(T, 1, H, 0, 1)[0] == rn.RMSN_FORM_PAIR
+    print(T, H, run_gated(Layout.plain(T, H), "bf16", seed=T + H + 5, kind="normal"))
+
+
 def test_gated_head_view():
     print(run_gated(Layout.heads_view(512, 24, 256, 8192, 256), "bf16", seed=3))
 
