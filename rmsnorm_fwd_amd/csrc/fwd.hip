@@ -79,6 +79,15 @@ __global__ void __launch_bounds__(block_of(LPR)) fwd_kernel(FwdParams p)
         }
     }
 
+    // Gated rows take sigmoid8 (the same bits as sigmoid_f32, fewer
+    // instructions) except where it was measured slower on MI355X: rows of
+    // one vector across several wavefronts with more than one row per lane
+    // (H 2048, 4096: it costs occupancy) and the 512-lane rows of one row
+    // (H 16384: not reliably faster).  Rows of two vectors and two rows
+    // (H 5120, 8192) take it together with the row sums reading one row's
+    // wavefront partials at a time (3-7 % and 2-4 % faster).
+    constexpr bool G2X2 = LPR >= 256 && V >= 2 && U >= 2;
+    constexpr bool SG8 = LPR < 256 || (LPR < 512 && U == 1) || G2X2;
     const int stride = gridDim.x * RPI;
     FwdTile<U, V, RES, GATE> cur;
     int it = 0;
@@ -119,7 +128,7 @@ __global__ void __launch_bounds__(block_of(LPR)) fwd_kernel(FwdParams p)
                 ss[u] += (double)(lv.ok[v] ? s : 0.f);
             }
         }
-        row_group_sum<LPR, U, RPI>(ss, red, it, slot, g);
+        row_group_sum<LPR, U, RPI, GATE && G2X2>(ss, red, it, slot, g);
 #pragma unroll
         for (int u = 0; u < U; ++u) {
             const float rs = rstd_from_ms(ss[u] * p.inv_h + p.eps);
@@ -137,14 +146,10 @@ __global__ void __launch_bounds__(block_of(LPR)) fwd_kernel(FwdParams p)
 #pragma unroll
                 for (int e = 0; e < 8; ++e) f[e] = (f[e] * rs) * wv[e];
                 if constexpr (GATE) {
-                    // y = (u * rstd * w) * silu(g), all in FP32.  sigmoid8
-                    // (same bits as sigmoid_f32) is slower where a row spans
-                    // several wavefronts and a lane holds more than one row
-                    // (measured on MI355X: H 2048, 4096, 8192) and not
-                    // reliably faster on the 512-lane rows (H 16384).
+                    // y = (u * rstd * w) * silu(g), all in FP32.
                     float gf[8], sgv[8];
                     unpack8(cur.rv[u][v], gf);
-                    if constexpr (LPR >= 512 || (LPR >= 256 && U > 1)) {
+                    if constexpr (!SG8) {
 #pragma unroll
                         for (int e = 0; e < 8; ++e) sgv[e] = sigmoid_f32(gf[e]);
                     } else {
