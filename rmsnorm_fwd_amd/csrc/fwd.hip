@@ -79,15 +79,12 @@ __global__ void __launch_bounds__(block_of(LPR)) fwd_kernel(FwdParams p)
         }
     }
 
-    // Gated rows take sigmoid8 (the same bits as sigmoid_f32, fewer
-    // instructions) except where it was measured slower on MI355X: rows of
-    // one vector across several wavefronts with more than one row per lane
-    // (H 2048, 4096: it costs occupancy) and the 512-lane rows of one row
-    // (H 16384: not reliably faster).  Rows of two vectors and two rows
-    // (H 5120, 8192) take it together with the row sums reading one row's
-    // wavefront partials at a time (3-7 % and 2-4 % faster).
-    constexpr bool G2X2 = LPR >= 256 && V >= 2 && U >= 2;
-    constexpr bool SG8 = LPR < 256 || (LPR < 512 && U == 1) || G2X2;
+    // Gated rows up to 8192 wide take sigmoid8 (the same bits as
+    // sigmoid_f32, fewer instructions), with the row sums reading one row's
+    // wavefront partials at a time; the gated table's row layouts were
+    // measured with both.  Wider rows (H 16384) were not reliably faster
+    // with them.
+    constexpr bool SG8 = LPR * V * 8 <= 8192;
     const int stride = gridDim.x * RPI;
     FwdTile<U, V, RES, GATE> cur;
     int it = 0;
@@ -128,7 +125,7 @@ __global__ void __launch_bounds__(block_of(LPR)) fwd_kernel(FwdParams p)
                 ss[u] += (double)(lv.ok[v] ? s : 0.f);
             }
         }
-        row_group_sum<LPR, U, RPI, GATE && G2X2>(ss, red, it, slot, g);
+        row_group_sum<LPR, U, RPI, GATE && SG8>(ss, red, it, slot, g);
 #pragma unroll
         for (int u = 0; u < U; ++u) {
             const float rs = rstd_from_ms(ss[u] * p.inv_h + p.eps);

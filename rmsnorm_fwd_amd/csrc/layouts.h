@@ -110,21 +110,25 @@ constexpr long long kFwdResLongRows = 32768;
     X(12, 16384, 512, 4, 1, 8)
 
 // The SiLU-gated forward is an operation of its own (its rstd need not equal
-// the plain forward's bits), with its own table: the plain one, except at
-// H 6144, where 256 lanes x 3 vectors and one row per row group beat the
-// plain 768 x 1 (T 65536: 421-425 against 473-478 us; T 16384: 102 against
-// 130 us; 384 x 2: 444 / 118).
+// the plain forward's bits), with its own table, measured on MI355X with the
+// eight-gate sigmoid (cold, T 4096-131072, BF16 and FP32 w): one row per row
+// group of two to four vectors per lane from H 1024 to 5120 (T 65536, H 2048:
+// 146 -> 130 us; H 4096: 279 -> 257 us, 128 x 4 beating 256 x 2 from 65536
+// rows; H 5120: 389 -> 362 us), 256 lanes x 3 vectors at H 6144 (T 65536:
+// 421-425 against 473-478 us for 768 x 1; 384 x 2: 444 us), and the plain
+// table's layouts at H 3072 and 8192 (the alternatives measured there were
+// not faster at every row count).
 #define RMSN_FWD_GATED_LAYOUTS(X) \
     X(0, 64, 8, 1, 4, 64)         \
     X(1, 128, 16, 1, 4, 64)       \
     X(2, 256, 8, 4, 1, 64)        \
     X(3, 512, 32, 2, 2, 64)       \
-    X(4, 1024, 32, 4, 1, 64)      \
-    X(5, 1536, 32, 6, 1, 16)      \
-    X(6, 2048, 256, 1, 4, 64)     \
+    X(4, 1024, 64, 2, 1, 64)      \
+    X(5, 1536, 64, 3, 1, 64)      \
+    X(6, 2048, 128, 2, 1, 64)     \
     X(7, 3072, 64, 6, 1, 32)      \
-    X(8, 4096, 512, 1, 2, 64)     \
-    X(9, 5120, 320, 2, 2, 64)     \
+    X(8, 4096, 128, 4, 1, 64)     \
+    X(9, 5120, 320, 2, 1, 64)     \
     X(10, 6144, 256, 3, 1, 32)    \
     X(11, 8192, 512, 2, 2, 32)    \
     X(12, 16384, 512, 4, 1, 8)
