@@ -117,7 +117,9 @@ constexpr long long kFwdResLongRows = 32768;
 // rows; H 5120: 389 -> 362 us), 256 lanes x 3 vectors at H 6144 (T 65536:
 // 421-425 against 473-478 us for 768 x 1; 384 x 2: 444 us), and the plain
 // table's layouts at H 3072 and 8192 (the alternatives measured there were
-// not faster at every row count).
+// not faster at every row count); 64 workgroups per compute unit at every
+// width up to 8192 (against 32 at H 3072-8192: T 65536, H 6144 423 -> 400
+// us, H 3072 200 -> 193 us; 16 was slower).
 #define RMSN_FWD_GATED_LAYOUTS(X) \
     X(0, 64, 8, 1, 4, 64)         \
     X(1, 128, 16, 1, 4, 64)       \
@@ -126,11 +128,11 @@ constexpr long long kFwdResLongRows = 32768;
     X(4, 1024, 64, 2, 1, 64)      \
     X(5, 1536, 64, 3, 1, 64)      \
     X(6, 2048, 128, 2, 1, 64)     \
-    X(7, 3072, 64, 6, 1, 32)      \
+    X(7, 3072, 64, 6, 1, 64)      \
     X(8, 4096, 128, 4, 1, 64)     \
     X(9, 5120, 320, 2, 1, 64)     \
-    X(10, 6144, 256, 3, 1, 32)    \
-    X(11, 8192, 512, 2, 2, 32)    \
+    X(10, 6144, 256, 3, 1, 64)    \
+    X(11, 8192, 512, 2, 2, 64)    \
     X(12, 16384, 512, 4, 1, 8)
 
 #define RMSN_BWD_LAYOUTS(X)       \
