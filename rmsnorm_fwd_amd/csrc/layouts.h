@@ -36,7 +36,9 @@ struct Layout {
 // H 2048: 91.3 -> 89.5 us) and equal below.  At H 6144 a larger cap pays
 // only in long runs (48: T 131072 548 -> 540 us), and was 2 % slower at
 // T 16384, so only the long-run table takes it; at H 1536 and 3072 it made
-// no difference.  A tuning build may
+// no difference.  At H 16384 both long-run tables take 32 instead of 8
+// (T 65536: 767 -> 731 us with FP32 w, 752 -> 739 us, residual 1641 -> 1605
+// us); at T 4096 it was mixed, so the plain table keeps 8.  A tuning build may
 // supply its own candidate tables (all four, and the two row thresholds) through
 // RMSN_LAYOUTS_OVERRIDE.
 #ifdef RMSN_LAYOUTS_OVERRIDE
@@ -78,7 +80,7 @@ constexpr long long kFwdLongRows = 65536;
     X(9, 5120, 320, 2, 3, 64)    \
     X(10, 6144, 768, 1, 2, 48)   \
     X(11, 8192, 512, 2, 2, 32)   \
-    X(12, 16384, 512, 4, 1, 8)
+    X(12, 16384, 512, 4, 1, 32)
 
 // The forward with a fused residual add streams four tensors (x, r in; h, y
 // out) instead of two.  Over at least kFwdResLongRows rows it keeps the plain
@@ -107,7 +109,7 @@ constexpr long long kFwdResLongRows = 32768;
     X(9, 5120, 320, 2, 4, 16)   \
     X(10, 6144, 768, 1, 4, 16)  \
     X(11, 8192, 512, 2, 2, 32)  \
-    X(12, 16384, 512, 4, 1, 8)
+    X(12, 16384, 512, 4, 1, 32)
 
 // The SiLU-gated forward is an operation of its own (its rstd need not equal
 // the plain forward's bits), with its own table, measured on MI355X with the

@@ -38,7 +38,7 @@ def test_residual(H, wdt, dres):
     print(H, wdt, dres, rep)
 
 
-@pytest.mark.parametrize("H", [1536, 4096, 5120, 6144])
+@pytest.mark.parametrize("H", [1536, 4096, 5120, 6144, 8192, 16384])
 def test_forward_tables_give_the_same_rows(H):
     # The plain forward takes another table from 65536 rows on, and the
     # residual forward another from 32768 rows on; all keep the row layout, so
