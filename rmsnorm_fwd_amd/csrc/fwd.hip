@@ -79,12 +79,6 @@ __global__ void __launch_bounds__(block_of(LPR)) fwd_kernel(FwdParams p)
         }
     }
 
-    // Gated rows up to 8192 wide take sigmoid8 (the same bits as
-    // sigmoid_f32, fewer instructions), with the row sums reading one row's
-    // wavefront partials at a time; the gated table's row layouts were
-    // measured with both.  Wider rows (H 16384) were not reliably faster
-    // with them.
-    constexpr bool SG8 = LPR * V * 8 <= 8192;
     const int stride = gridDim.x * RPI;
     FwdTile<U, V, RES, GATE> cur;
     int it = 0;
@@ -125,7 +119,9 @@ __global__ void __launch_bounds__(block_of(LPR)) fwd_kernel(FwdParams p)
                 ss[u] += (double)(lv.ok[v] ? s : 0.f);
             }
         }
-        row_group_sum<LPR, U, RPI, GATE && SG8>(ss, red, it, slot, g);
+        // gated rows read one row's wavefront partials at a time (fewer registers;
+        // the gated table's row layouts were measured with it)
+        row_group_sum<LPR, U, RPI, GATE>(ss, red, it, slot, g);
 #pragma unroll
         for (int u = 0; u < U; ++u) {
             const float rs = rstd_from_ms(ss[u] * p.inv_h + p.eps);
@@ -143,15 +139,11 @@ __global__ void __launch_bounds__(block_of(LPR)) fwd_kernel(FwdParams p)
 #pragma unroll
                 for (int e = 0; e < 8; ++e) f[e] = (f[e] * rs) * wv[e];
                 if constexpr (GATE) {
-                    // y = (u * rstd * w) * silu(g), all in FP32.
+                    // y = (u * rstd * w) * silu(g), all in FP32; sigmoid8
+                    // gives sigmoid_f32's bits with fewer instructions
                     float gf[8], sgv[8];
                     unpack8(cur.rv[u][v], gf);
-                    if constexpr (!SG8) {
-#pragma unroll
-                        for (int e = 0; e < 8; ++e) sgv[e] = sigmoid_f32(gf[e]);
-                    } else {
-                        sigmoid8(gf, sgv);
-                    }
+                    sigmoid8(gf, sgv);
 #pragma unroll
                     for (int e = 0; e < 8; ++e) f[e] *= gf[e] * sgv[e];
                 }

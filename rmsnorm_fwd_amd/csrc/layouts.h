@@ -121,7 +121,8 @@ constexpr long long kFwdResLongRows = 32768;
 // table's layouts at H 3072 and 8192 (the alternatives measured there were
 // not faster at every row count); 64 workgroups per compute unit at every
 // width up to 8192 (against 32 at H 3072-8192: T 65536, H 6144 423 -> 400
-// us, H 3072 200 -> 193 us; 16 was slower).
+// us, H 3072 200 -> 193 us; 16 was slower), 32 at H 16384 (against 8, with
+// the eight-gate sigmoid: T 4096 78 -> 73 us, T 65536 1128 -> 1096 us).
 #define RMSN_FWD_GATED_LAYOUTS(X) \
     X(0, 64, 8, 1, 4, 64)         \
     X(1, 128, 16, 1, 4, 64)       \
@@ -135,7 +136,7 @@ constexpr long long kFwdResLongRows = 32768;
     X(9, 5120, 320, 2, 1, 64)     \
     X(10, 6144, 256, 3, 1, 64)    \
     X(11, 8192, 512, 2, 2, 64)    \
-    X(12, 16384, 512, 4, 1, 8)
+    X(12, 16384, 512, 4, 1, 32)
 
 #define RMSN_BWD_LAYOUTS(X)       \
     X(0, 64, 8, 1, 2, 512)        \
